@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark: one rank's local-shard ring attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--gpus 1]
+
+A step is one pass of the whole hot path over resident inputs: the ring
+schedule, every non-skipped key/value block folded into the running softmax
+state in ring order, and the finalisation into out/lse -- one call of
+cakv_local_shard_forward (config 2: one call per rank, all four ranks). The
+default workload is the million-token causal context (T = 1,048,576 in 8
+chunks, rank 7, 32 query heads over 8 key/value heads, d_k = 128, bf16).
+
+Printed: ONE JSON line. value = useful TFLOP/s (4 d_k FLOPs per allowed
+(query, key) pair, masked work not counted) over the timed steps; roofline =
+the forward kernel's useful FLOPs per launch over its HIP-event-timed launch
+duration against the bf16 dense matrix peak (256 CUs x 2.4 GHz x 4096
+FLOP/clk = 2516.6 TFLOP/s); cpu_baseline = the fp64 CPU oracle timed on a
+bounded row sample on this host's cores (its rows double as a parity spot
+check, reported under "parity"); kernels = the bandwidth-bound finalize and
+log-sum-exp merge kernels timed at this workload's row count against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12      # 2516.58
+PEAK_F32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "local-shard attention TFLOP/s (useful causal FLOPs), % of bf16 MFMA peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "fwd_bf16.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def allowed_pairs(w, rank: int) -> int:
+    """Allowed (query, key) pairs per (batch, query head) of one rank: every
+    earlier chunk in full plus the lower triangle (diagonal included) of its
+    own chunk when causal; all N*C*C pairs when bidirectional."""
+    C = w.C
+    if not w.causal:
+        return w.N * C * C
+    return rank * C * C + C * (C + 1) // 2
+
+
+def useful_flops(w, ranks) -> int:
+    return sum(4 * w.D * allowed_pairs(w, r) * w.B * w.Hq for r in ranks)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload_name: str):
+    """HBM bytes per launch of the forward kernel from the committed counter
+    profile, if it was taken on this workload and on the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the CPU oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one rank's share on ONE GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: the ring over several GPUs is not "
+              "built, only the single-GPU hot path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import cakv_synth as syn
+    import context_attention_kv_amd as cakv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = syn.WORKLOADS[args.config]
+    ranks = list(w.ranks)
+    C = w.C
+
+    # ---- inputs: seeded on the host, then resident in HBM -----------------
+    t0 = time.time()
+    log(f"generating {w.name}")
+    k_host = syn.make_kv_full(w, "k")
+    v_host = syn.make_kv_full(w, "v")
+    q_host = {r: syn.make_q_local(w, r) for r in ranks}
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    kd, vd = dev(k_host), dev(v_host)
+    if w.B == 1:
+        kb = [kd[:, j * C:(j + 1) * C] for j in range(w.N)]
+        vb = [vd[:, j * C:(j + 1) * C] for j in range(w.N)]
+    else:
+        kb = [kd[:, j * C:(j + 1) * C].contiguous() for j in range(w.N)]
+        vb = [vd[:, j * C:(j + 1) * C].contiguous() for j in range(w.N)]
+        del kd, vd
+    qd = {r: dev(q_host[r]) for r in ranks}
+    out = {r: torch.empty((w.B, C, w.Hq, w.D), dtype=torch.float32, device="cuda") for r in ranks}
+    lse = {r: torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda") for r in ranks}
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    n_launch = len(ranks)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n_launch)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n_launch)]
+
+    def step(timed_idx=None):
+        for i, r in enumerate(ranks):
+            if timed_idx is not None:
+                starts[timed_idx * n_launch + i].record(stream)
+            cakv.cakv_local_shard_forward(qd[r], kb, vb, r, w.causal, out[r], lse[r])
+            if timed_idx is not None:
+                ends[timed_idx * n_launch + i].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(s)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    log("timed steps done")
+
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    flops_step = useful_flops(w, ranks)
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    # per-launch useful FLOPs: each launch is one rank's shard
+    per_launch = [useful_flops(w, [r]) for r in ranks] * args.steps
+    achieved = sum(per_launch) / (sum(launch_ms) * 1e-3) / 1e12
+    is_bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_F32_VALU_TFLOPS
+    traffic = traffic_for(w.name)
+    roofline = {
+        "bound": "mfma" if is_bf16 else "alu",
+        "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
+        "achieved": round(achieved, 2),
+        "peak": round(peak, 1),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic,
+        "avg_launch_ms": round(sum(launch_ms) / len(launch_ms), 4),
+        "flops_per_launch": per_launch[0] if len(set(per_launch)) == 1 else None,
+    }
+
+    # ---- bandwidth-bound kernels at this workload's row count ---------------
+    kernels = {}
+    if not args.no_aux:
+        r = ranks[-1]
+        rows = w.B * w.Hq * C
+        o_a = out[r]
+        o_b = torch.empty_like(o_a).copy_(o_a)
+        l_a, l_b = lse[r], lse[r].clone()
+        o_o = torch.empty_like(o_a)
+        l_o = torch.empty_like(l_a)
+        l_state = torch.ones_like(l_a)
+        fin = torch.empty_like(o_a)
+
+        def timeit(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for a, b in ev:
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+            return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+        t_fin = timeit(lambda: cakv.cakv_finalize(l_a, l_state, o_a, fin, l_o))
+        t_mrg = timeit(lambda: cakv.cakv_lse_merge(o_a, l_a, o_b, l_b, o_o, l_o))
+        b_fin = rows * (8 * w.D + 12)
+        b_mrg = rows * (12 * w.D + 12)
+        kernels = {
+            "finalize": {"bound": "hbm", "ms": round(t_fin, 4), "bytes": b_fin,
+                         "achieved_GBs": round(b_fin / t_fin / 1e6, 1), "peak_GBs": PEAK_HBM_GBS,
+                         "frac": round(b_fin / t_fin / 1e6 / PEAK_HBM_GBS, 4)},
+            "lse_merge": {"bound": "hbm", "ms": round(t_mrg, 4), "bytes": b_mrg,
+                          "achieved_GBs": round(b_mrg / t_mrg / 1e6, 1), "peak_GBs": PEAK_HBM_GBS,
+                          "frac": round(b_mrg / t_mrg / 1e6 / PEAK_HBM_GBS, 4)},
+        }
+        del o_b, o_o, fin
+        log("finalize/merge timed")
+
+    # ---- CPU oracle baseline on a bounded row sample (also a parity check) --
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        r = ranks[-1]
+        sample = syn.sample_rows(w, per_head=16, seed=11)
+        rng = np.random.default_rng(11)
+        sample = sample[rng.permutation(len(sample))]
+        done, spent, flops_cpu = 0, 0.0, 0
+        got_o_all, ref_o_all, got_l_all, ref_l_all = [], [], [], []
+        o_host = out[r].cpu().numpy()
+        l_host = lse[r].cpu().numpy()
+        batch = max(cores, 8)
+        while done < len(sample) and spent < args.cpu_seconds:
+            rows = sample[done:done + batch]
+            t = time.perf_counter()
+            ro, rl = oracle.attention(q_host[r], k_host, v_host, q_off=r * C, causal=w.causal,
+                                      rows=rows, threads=cores)
+            spent += time.perf_counter() - t
+            for (b, h, i) in rows:
+                keys = (r * C + i + 1) if w.causal else w.T
+                flops_cpu += 4 * w.D * keys
+            got_o_all.append(o_host[rows[:, 0], rows[:, 2], rows[:, 1]])
+            got_l_all.append(l_host[rows[:, 0], rows[:, 1], rows[:, 2]])
+            ref_o_all.append(ro)
+            ref_l_all.append(rl)
+            done += len(rows)
+        cpu_tflops = flops_cpu / spent / 1e12
+        cpu_baseline = {
+            "value": cpu_tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} query rows (seeded, all heads) of rank {r}'s shard, fp64, "
+                      f"{spent:.1f}s; full shard extrapolated "
+                      f"{useful_flops(w, [r]) / (cpu_tflops * 1e12):.0f}s",
+        }
+        go = np.concatenate(got_o_all)
+        ro = np.concatenate(ref_o_all)
+        gl = np.concatenate(got_l_all)
+        rl = np.concatenate(ref_l_all)
+        parity = {"rows": int(done), "max_abs_out": float(np.abs(go - ro).max()),
+                  "mean_abs_out": float(np.abs(go - ro).mean()),
+                  "max_abs_lse": float(np.abs(gl - rl).max())}
+        log(f"cpu baseline: {done} rows in {spent:.1f}s")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if is_bf16 else "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T,
+                   "N": w.N, "chunk": C, "d_k": w.D, "causal": w.causal, "ranks": ranks,
+                   "parallelism": "one context-parallel rank's share on 1 GPU"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity": parity,
+        "kernels": kernels,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""Python binding of libcakv: local-shard ring attention on MI355X (gfx950).
+
+Argument marshalling only. Every function here has the name and meaning of a
+C entry point declared in include/cakv.h; it turns torch tensors into device
+pointers and the current HIP stream into a handle, calls libcakv.so through
+ctypes, and raises CakvError on a non-zero status. All device work happens in
+the library's HIP kernels; there is no fallback. If libcakv.so is missing the
+import fails: build it with ``python -m context_attention_kv_amd.build``.
+
+Layouts (contiguous, innermost last): Q/out/o [B, T, Hq, D]; K/V blocks
+[B, T, Hkv, D]; m/l/lse [B, Hq, T].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcakv.so")
+
+CAKV_OK = 0
+CAKV_F32, CAKV_BF16 = 0, 1
+CAKV_FULL, CAKV_DIAG, CAKV_SKIP = 0, 1, 2
+CAKV_MAX_CHUNKS = 64
+CAKV_TILE_Q, CAKV_TILE_K = 32, 64
+
+# every symbol include/cakv.h declares
+EXPORTED = (
+    "cakv_abi_version", "cakv_status_str", "cakv_last_error", "cakv_classify_block",
+    "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
+    "cakv_lse_merge", "cakv_local_shard_forward",
+)
+
+
+class CakvError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        super().__init__(f"{func}: {status_str(status)}: {detail}")
+
+
+def _load_lib():
+    # torch ships its own HIP runtime under the same soname; loading it first
+    # makes libcakv bind to that one instance, so tensors, streams and kernels
+    # all live in a single runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libcakv.so not found at {LIB_PATH}; build it with "
+            "`python -m context_attention_kv_amd.build` (needs ROCm hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "cakv_abi_version": ([], I),
+        "cakv_status_str": ([I], ctypes.c_char_p),
+        "cakv_last_error": ([], ctypes.c_char_p),
+        "cakv_classify_block": ([I64, I64, I64, I64, I, P], I),
+        "cakv_schedule": ([I, I, I64, I, P, P], I),
+        "cakv_state_init": ([P, P, P, I, I, I, I, P], I),
+        "cakv_block_update": ([P, P, P, I, I, I, I, I, I, I, I64, I64, I, F, P, P, P, P, P], I),
+        "cakv_finalize": ([P, P, P, P, I, P, I, I, I, I, P], I),
+        "cakv_lse_merge": ([P, P, P, P, P, P, I, I, I, I, P], I),
+        "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load_lib()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return _lib.cakv_status_str(status).decode()
+
+
+def _check(status: int, func: str):
+    if status != CAKV_OK:
+        raise CakvError(status, func, _lib.cakv_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CAKV_BF16
+    if t.dtype == torch.float32:
+        return CAKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def abi_version() -> int:
+    return _lib.cakv_abi_version()
+
+
+def cakv_classify_block(q_offset: int, q_len: int, kv_offset: int, kv_len: int,
+                        causal: bool) -> int:
+    out = ctypes.c_int8()
+    _check(_lib.cakv_classify_block(q_offset, q_len, kv_offset, kv_len, int(causal),
+                                    ctypes.byref(out)), "cakv_classify_block")
+    return out.value
+
+
+def cakv_schedule(rank: int, n_chunks: int, chunk_len: int, causal: bool):
+    """Ring order and per-block class for one rank (host only)."""
+    n = max(int(n_chunks), 0)
+    blocks = (ctypes.c_int32 * max(n, 1))()
+    classes = (ctypes.c_int8 * max(n, 1))()
+    _check(_lib.cakv_schedule(rank, n_chunks, chunk_len, int(causal), blocks, classes),
+           "cakv_schedule")
+    return list(blocks[:n]), list(classes[:n])
+
+
+def cakv_state_init(m, l, o, stream=None):
+    _contig(m, l, o)
+    B, Tq, Hq, D = o.shape
+    _check(_lib.cakv_state_init(_ptr(m), _ptr(l), _ptr(o), B, Hq, Tq, D, _stream(stream)),
+           "cakv_state_init")
+
+
+def cakv_block_update(q, k, v, q_offset: int, kv_offset: int, causal: bool, m, l, o,
+                      scale: float = 0.0, tile_counters=None, stream=None):
+    _contig(q, k, v, m, l, o)
+    B, Tq, Hq, D = q.shape
+    Bk, Tkv, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape) or v.dtype != k.dtype \
+            or q.dtype != k.dtype:
+        raise ValueError("q/k/v shapes or dtypes disagree")
+    if tuple(o.shape) != (B, Tq, Hq, D) or tuple(m.shape) != (B, Hq, Tq) \
+            or tuple(l.shape) != (B, Hq, Tq):
+        raise ValueError("state shapes disagree with q")
+    _check(_lib.cakv_block_update(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Tq,
+                                  Tkv, D, q_offset, kv_offset, int(causal), float(scale),
+                                  _ptr(m), _ptr(l), _ptr(o), _ptr(tile_counters),
+                                  _stream(stream)), "cakv_block_update")
+
+
+def cakv_finalize(m, l, o, out, lse=None, stream=None):
+    _contig(m, l, o, out, lse)
+    B, Tq, Hq, D = o.shape
+    if tuple(out.shape) != tuple(o.shape):
+        raise ValueError("out shape disagrees with o")
+    _check(_lib.cakv_finalize(_ptr(m), _ptr(l), _ptr(o), _ptr(out), _dtype_code(out),
+                              _ptr(lse), B, Hq, Tq, D, _stream(stream)), "cakv_finalize")
+
+
+def cakv_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
+    _contig(o_a, lse_a, o_b, lse_b, o_out, lse_out)
+    B, Tq, Hq, D = o_a.shape
+    for t in (o_b, o_out):
+        if tuple(t.shape) != tuple(o_a.shape):
+            raise ValueError("merge operand shapes disagree")
+    _check(_lib.cakv_lse_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o_out),
+                               _ptr(lse_out), B, Hq, Tq, D, _stream(stream)), "cakv_lse_merge")
+
+
+def cakv_local_shard_forward(q_local, k_blocks: Sequence, v_blocks: Sequence, rank: int,
+                             causal: bool, out, lse=None, scale: float = 0.0,
+                             tile_counters=None, stream=None):
+    """One rank's share: q_local [B, C, Hq, D] against N blocks [B, C, Hkv, D]
+    in ring order rank, rank-1, ...; writes out [B, C, Hq, D] and lse [B, Hq, C]."""
+    _contig(q_local, out, lse, *k_blocks, *v_blocks)
+    B, C, Hq, D = q_local.shape
+    n = len(k_blocks)
+    if len(v_blocks) != n or n == 0:
+        raise ValueError("need the same positive number of K and V blocks")
+    Hkv = k_blocks[0].shape[2]
+    for t in list(k_blocks) + list(v_blocks):
+        if tuple(t.shape) != (B, C, Hkv, D) or t.dtype != q_local.dtype:
+            raise ValueError("every block must be [B, C, Hkv, D] with the query dtype")
+    karr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_blocks])
+    varr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_blocks])
+    _check(_lib.cakv_local_shard_forward(_ptr(q_local), karr, varr, _dtype_code(q_local), B,
+                                         Hq, Hkv, C, n, D, rank, int(causal), float(scale),
+                                         _ptr(out), _dtype_code(out), _ptr(lse),
+                                         _ptr(tile_counters), _stream(stream)),
+           "cakv_local_shard_forward")

@@ -1,0 +1,279 @@
+// api.cpp -- the C ABI of libcakv: argument checks, the ring schedule, and the
+// launch of the kernels. Declarations, layouts and error rules: include/cakv.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "cakv.h"
+#include "fwd_args.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+cakv_status fail(cakv_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+cakv_status ok() {
+    g_err.clear();
+    return CAKV_OK;
+}
+
+cakv_status hip_status(int err, const char* what) {
+    if (err == (int)hipSuccess) return ok();
+    return fail(CAKV_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tuning override for the bf16 kernel: query rows per wave (32 or 64).
+int rows_per_wave() {
+    static const int v = [] {
+        const char* e = std::getenv("CAKV_ROWS_PER_WAVE");
+        if (e && std::atoi(e) == 64) return 64;
+        return 32;
+    }();
+    return v;
+}
+
+cakv_class classify(int64_t q_off, int64_t q_len, int64_t kv_off, int64_t kv_len, int causal) {
+    if (q_len <= 0 || kv_len <= 0) return CAKV_SKIP;
+    if (!causal) return CAKV_FULL;
+    const int64_t q_last = q_off + q_len - 1, kv_last = kv_off + kv_len - 1;
+    if (kv_off > q_last) return CAKV_SKIP;
+    if (kv_last <= q_off) return CAKV_FULL;
+    return CAKV_DIAG;
+}
+
+cakv_status check_common(int dtype, int B, int Hq, int Hkv, int Tq, int Tkv, int D) {
+    if (dtype != CAKV_F32 && dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "dtype %d is neither CAKV_F32 nor CAKV_BF16", dtype);
+    if (B < 0 || Tq < 0 || Tkv < 0)
+        return fail(CAKV_ERR_SHAPE, "negative size (B=%d Tq=%d Tkv=%d)", B, Tq, Tkv);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(CAKV_ERR_SHAPE, "heads must be positive with Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                    Hq, Hkv);
+    if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    return CAKV_OK;
+}
+
+float resolve_scale(float scale, int D) {
+    return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+}
+
+// Fill the workgroup geometry of a forward launch.
+void set_grid(cakv::FwdArgs& a, int dtype, int D) {
+    (void)D;
+    if (dtype == CAKV_BF16) {
+        const int rw = rows_per_wave();
+        const int G = a.Hq / a.Hkv;
+        const long long npblk = (a.Tq + rw - 1) / rw;
+        a.wg_per_bg = (int)((G * npblk + 3) / 4);
+        a.n_wg = (int)((long long)a.B * a.Hkv * a.wg_per_bg);
+    } else {
+        const int rows = cakv::fwd_f32_wg_rows();
+        a.wg_per_bg = (a.Tq + rows - 1) / rows;
+        a.n_wg = (int)((long long)a.B * a.Hq * a.wg_per_bg);
+    }
+}
+
+int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
+    if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, rows_per_wave(), stream);
+    return cakv::launch_fwd_f32(a, D, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cakv_abi_version(void) { return CAKV_ABI_VERSION; }
+
+const char* cakv_status_str(int status) {
+    switch (status) {
+        case CAKV_OK: return "CAKV_OK";
+        case CAKV_ERR_NULL: return "CAKV_ERR_NULL";
+        case CAKV_ERR_SHAPE: return "CAKV_ERR_SHAPE";
+        case CAKV_ERR_DTYPE: return "CAKV_ERR_DTYPE";
+        case CAKV_ERR_ALIGN: return "CAKV_ERR_ALIGN";
+        case CAKV_ERR_RANGE: return "CAKV_ERR_RANGE";
+        case CAKV_ERR_HIP: return "CAKV_ERR_HIP";
+        case CAKV_ERR_INTERNAL: return "CAKV_ERR_INTERNAL";
+        default: return "CAKV_UNKNOWN_STATUS";
+    }
+}
+
+const char* cakv_last_error(void) { return g_err.c_str(); }
+
+cakv_status cakv_classify_block(int64_t q_offset, int64_t q_len, int64_t kv_offset,
+                                int64_t kv_len, int causal, int8_t* class_host) {
+    if (!class_host) return fail(CAKV_ERR_NULL, "class_host is NULL");
+    if (q_len < 0 || kv_len < 0) return fail(CAKV_ERR_SHAPE, "negative length");
+    *class_host = (int8_t)classify(q_offset, q_len, kv_offset, kv_len, causal);
+    return ok();
+}
+
+cakv_status cakv_schedule(int rank, int n_chunks, int64_t chunk_len, int causal,
+                          int32_t* blocks_host, int8_t* class_host) {
+    if (!blocks_host || !class_host) return fail(CAKV_ERR_NULL, "output array is NULL");
+    if (n_chunks < 1 || n_chunks > CAKV_MAX_CHUNKS)
+        return fail(CAKV_ERR_RANGE, "n_chunks=%d outside [1, %d]", n_chunks, CAKV_MAX_CHUNKS);
+    if (rank < 0 || rank >= n_chunks)
+        return fail(CAKV_ERR_RANGE, "rank=%d outside [0, %d)", rank, n_chunks);
+    if (chunk_len < 0) return fail(CAKV_ERR_SHAPE, "chunk_len=%lld < 0", (long long)chunk_len);
+    for (int k = 0; k < n_chunks; ++k) {
+        const int j = ((rank - k) % n_chunks + n_chunks) % n_chunks;
+        blocks_host[k] = j;
+        class_host[k] = (int8_t)classify((int64_t)rank * chunk_len, chunk_len,
+                                         (int64_t)j * chunk_len, chunk_len, causal);
+    }
+    return ok();
+}
+
+cakv_status cakv_state_init(float* m, float* l, float* o, int B, int Hq, int Tq, int D,
+                            void* stream) {
+    if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
+    if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    const long long rows = (long long)B * Hq * Tq;
+    if (rows == 0) return ok();
+    if (!m || !l || !o) return fail(CAKV_ERR_NULL, "state pointer is NULL");
+    if (!aligned16(o)) return fail(CAKV_ERR_ALIGN, "o not 16-byte aligned");
+    return hip_status(cakv::launch_state_init(m, l, o, rows, D, stream), "state_init launch");
+}
+
+cakv_status cakv_block_update(const void* q, const void* k, const void* v, int dtype, int B,
+                              int Hq, int Hkv, int Tq, int Tkv, int D, int64_t q_offset,
+                              int64_t kv_offset, int causal, float scale, float* m, float* l,
+                              float* o, int64_t* tile_counters, void* stream) {
+    cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, Tkv, D);
+    if (s != CAKV_OK) return s;
+    if (B == 0 || Tq == 0) return ok();
+    if (!q || !m || !l || !o) return fail(CAKV_ERR_NULL, "q or state pointer is NULL");
+    if (Tkv > 0 && (!k || !v)) return fail(CAKV_ERR_NULL, "k or v is NULL");
+    if (!aligned16(q) || !aligned16(o) || (Tkv > 0 && (!aligned16(k) || !aligned16(v))))
+        return fail(CAKV_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
+    if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
+        return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
+    if (classify(q_offset, Tq, kv_offset, Tkv, causal) == CAKV_SKIP) return ok();
+
+    cakv::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = q;
+    a.k[0] = k;
+    a.v[0] = v;
+    a.kv_off[0] = kv_offset;
+    a.kv_len[0] = Tkv;
+    a.n_blocks = 1;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq;
+    a.q_off = q_offset;
+    a.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    a.causal = causal ? 1 : 0;
+    a.m = m; a.l = l; a.o = o;
+    a.load_state = 1;
+    a.store_state = 1;
+    a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
+    set_grid(a, dtype, D);
+    return hip_status(launch_fwd(a, dtype, D, stream), "block_update launch");
+}
+
+cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* out,
+                          int out_dtype, float* lse, int B, int Hq, int Tq, int D, void* stream) {
+    if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
+    if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
+    if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    if ((long long)B * Hq * Tq == 0) return ok();
+    if (!m || !l || !o || !out) return fail(CAKV_ERR_NULL, "m, l, o or out is NULL");
+    if (!aligned16(o) || !aligned16(out)) return fail(CAKV_ERR_ALIGN, "o/out not 16-byte aligned");
+    return hip_status(cakv::launch_finalize(m, l, o, out, out_dtype == CAKV_BF16, lse, B, Hq, Tq,
+                                            D, stream),
+                      "finalize launch");
+}
+
+cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_b,
+                           const float* lse_b, float* o_out, float* lse_out, int B, int Hq,
+                           int Tq, int D, void* stream) {
+    if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
+    if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    if ((long long)B * Hq * Tq == 0) return ok();
+    if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out)
+        return fail(CAKV_ERR_NULL, "merge operand is NULL");
+    if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out))
+        return fail(CAKV_ERR_ALIGN, "o operands must be 16-byte aligned");
+    return hip_status(cakv::launch_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, B, Hq, Tq, D,
+                                             stream),
+                      "lse_merge launch");
+}
+
+cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_blocks_host,
+                                     const void* const* v_blocks_host, int dtype, int B,
+                                     int Hq, int Hkv, int chunk_len, int n_chunks, int D,
+                                     int rank, int causal, float scale, void* out,
+                                     int out_dtype, float* lse, int64_t* tile_counters,
+                                     void* stream) {
+    cakv_status s = check_common(dtype, B, Hq, Hkv, chunk_len, chunk_len, D);
+    if (s != CAKV_OK) return s;
+    if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
+    if (n_chunks < 1 || n_chunks > CAKV_MAX_CHUNKS)
+        return fail(CAKV_ERR_RANGE, "n_chunks=%d outside [1, %d]", n_chunks, CAKV_MAX_CHUNKS);
+    if (rank < 0 || rank >= n_chunks)
+        return fail(CAKV_ERR_RANGE, "rank=%d outside [0, %d)", rank, n_chunks);
+    if (B == 0 || chunk_len == 0) return ok();
+    if (!q_local || !out) return fail(CAKV_ERR_NULL, "q_local or out is NULL");
+    if (!k_blocks_host || !v_blocks_host) return fail(CAKV_ERR_NULL, "block pointer array is NULL");
+    if (!aligned16(q_local) || !aligned16(out))
+        return fail(CAKV_ERR_ALIGN, "q_local/out not 16-byte aligned");
+    if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
+        return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
+
+    int32_t order[CAKV_MAX_CHUNKS];
+    int8_t cls[CAKV_MAX_CHUNKS];
+    s = cakv_schedule(rank, n_chunks, chunk_len, causal, order, cls);
+    if (s != CAKV_OK) return s;
+
+    cakv::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    int n = 0;
+    for (int t = 0; t < n_chunks; ++t) {
+        if (cls[t] == CAKV_SKIP) continue;
+        const int j = order[t];
+        const void* kp = k_blocks_host[j];
+        const void* vp = v_blocks_host[j];
+        if (!kp || !vp) return fail(CAKV_ERR_NULL, "block %d pointer is NULL", j);
+        if (!aligned16(kp) || !aligned16(vp))
+            return fail(CAKV_ERR_ALIGN, "block %d not 16-byte aligned", j);
+        a.k[n] = kp;
+        a.v[n] = vp;
+        a.kv_off[n] = (long long)j * chunk_len;
+        a.kv_len[n] = chunk_len;
+        ++n;
+    }
+    a.q = q_local;
+    a.n_blocks = n;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = chunk_len;
+    a.q_off = (long long)rank * chunk_len;
+    a.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    a.causal = causal ? 1 : 0;
+    a.load_state = 0;
+    a.store_state = 0;
+    a.out = out;
+    a.out_bf16 = out_dtype == CAKV_BF16;
+    a.lse = lse;
+    a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
+    set_grid(a, dtype, D);
+    return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
+}
+
+}  // extern "C"

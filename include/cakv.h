@@ -1,0 +1,201 @@
+/*
+ * cakv.h -- C ABI of the local-shard ring attention library (libcakv.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. Source: web page "Sequence parallelism -- splitting the
+ * token dimension across GPUs" (llmdaily.org, day 58).
+ *   - A sequence of T tokens is cut into N contiguous chunks of C = T/N
+ *     tokens; rank r owns positions [r*C, (r+1)*C) (section "Split tokens
+ *     across four GPUs"; positions here are 0-based).
+ *   - Rank r keeps its queries in place while key/value blocks arrive one at
+ *     a time (section "A better mental model: move blocks past the queries").
+ *     On one GPU the blocks already sit in device memory and the "ring" is the
+ *     order in which they are consumed: r, r-1, ..., wrapping modulo N.
+ *   - Each query row computes softmax(q K^T / sqrt(d_k)) V (section
+ *     "Attention wants keys and values from other tokens") without ever
+ *     holding a full score row: a running max m, normaliser l and value
+ *     accumulator o are rescaled and merged per block (section "But softmax
+ *     seems to require all attention scores at once").
+ *   - Under a causal mask a query sees keys at positions <= its own; blocks
+ *     entirely in the future are skipped and only blocks straddling the
+ *     diagonal are masked (section "Causal attention gives us another
+ *     optimization").
+ *   - Partial results over disjoint key sets are combined (section "Training
+ *     and inference stress this dimension differently"); here by the
+ *     log-sum-exp merge of normalised pairs (o, lse).
+ *
+ * Conventions for every call.
+ *   - Pointers are DEVICE pointers owned by the caller unless marked "host".
+ *     The library never allocates, frees or synchronises device memory; all
+ *     device work is enqueued asynchronously on `stream` (a hipStream_t cast
+ *     to void*, NULL = the default stream).
+ *   - Layouts (row-major, innermost dimension last, contiguous):
+ *       Q, out, o        [B, Tq, Hq, D]
+ *       K, V (one block) [B, Tkv, Hkv, D]
+ *       m, l, lse        [B, Hq, Tq]
+ *     Query head h reads key/value head h / (Hq / Hkv).
+ *   - Running state: m = running maximum of the scaled scores s = q.k*scale
+ *     (natural units), l = sum of e^{s - m}, o = sum of e^{s - m} v (NOT
+ *     normalised). A row that has seen no allowed key has m = -inf, l = 0,
+ *     o = 0. Finalised results: out = o / l, lse = m + ln(l); a row with
+ *     l = 0 finalises to out = 0, lse = -inf.
+ *   - dtype: CAKV_BF16 inputs are multiplied on bf16 matrix cores with fp32
+ *     accumulation (probabilities are rounded to bf16 before P*V); CAKV_F32
+ *     inputs are computed in fp32 throughout. State, lse and merge operands
+ *     are always fp32.
+ *   - scale <= 0 selects 1/sqrt(D).
+ *   - Supported: D in {64, 128}; Hq % Hkv == 0; 16-byte aligned pointers;
+ *     sizes >= 0 (an empty problem returns CAKV_OK and launches nothing).
+ *   - Errors: arguments are checked before anything is enqueued; on an error
+ *     nothing is launched, outputs are untouched, the status is returned and
+ *     cakv_last_error() describes it. A failed kernel launch returns
+ *     CAKV_ERR_HIP. Faults inside kernels surface at the caller's next
+ *     synchronisation. No C++ exception crosses this interface.
+ *   - Thread safety: the library keeps no state besides the thread-local
+ *     error message; calls on different streams are independent. Calls that
+ *     write the same buffers must be ordered by the caller.
+ */
+#ifndef CAKV_H
+#define CAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CAKV_ABI_VERSION 1
+#define CAKV_MAX_CHUNKS 64 /* most key/value blocks one forward call takes */
+#define CAKV_TILE_Q 32     /* query rows per counted tile */
+#define CAKV_TILE_K 64     /* keys per counted tile */
+
+typedef enum {
+    CAKV_OK = 0,
+    CAKV_ERR_NULL = 1,     /* a required pointer is NULL */
+    CAKV_ERR_SHAPE = 2,    /* negative size, unsupported D, Hq % Hkv != 0, ... */
+    CAKV_ERR_DTYPE = 3,    /* unknown dtype */
+    CAKV_ERR_ALIGN = 4,    /* pointer not 16-byte aligned */
+    CAKV_ERR_RANGE = 5,    /* rank / chunk count / offset out of range */
+    CAKV_ERR_HIP = 6,      /* the HIP runtime reported an error */
+    CAKV_ERR_INTERNAL = 7
+} cakv_status;
+
+typedef enum { CAKV_F32 = 0, CAKV_BF16 = 1 } cakv_dtype;
+
+/* class of a key/value block (or tile) relative to a query range */
+typedef enum {
+    CAKV_FULL = 0, /* every (query, key) pair is allowed: no mask */
+    CAKV_DIAG = 1, /* some pairs allowed: masked from global positions */
+    CAKV_SKIP = 2  /* no pair allowed (or nothing to pair): never read */
+} cakv_class;
+
+/* CAKV_ABI_VERSION of the loaded library. */
+int cakv_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* cakv_status_str(int status);
+
+/* Detail of the last error on this thread ("" if none). Valid until the next
+ * call from the same thread. */
+const char* cakv_last_error(void);
+
+/*
+ * Class of one block: keys at global positions [kv_offset, kv_offset+kv_len)
+ * against queries at [q_offset, q_offset+q_len). Causal: SKIP if the first
+ * key is after the last query (or either range is empty), FULL if the last
+ * key is at or before the first query, else DIAG. Bidirectional: FULL unless
+ * empty. Host only, pure. Page section "Causal attention gives us another
+ * optimization".
+ */
+cakv_status cakv_classify_block(int64_t q_offset, int64_t q_len, int64_t kv_offset,
+                                int64_t kv_len, int causal, int8_t* class_host);
+
+/*
+ * Ring schedule of rank `rank` of `n_chunks` equal chunks of `chunk_len`
+ * tokens: blocks_host[k] = (rank - k) mod n_chunks for k = 0..n_chunks-1 (the
+ * order the blocks pass the rank's stationary queries, page section "A better
+ * mental model: move blocks past the queries") and class_host[k] = class of
+ * that block for the rank's queries (cakv_classify_block). Host arrays of
+ * n_chunks entries, written by the call. Host only, pure.
+ * Errors: NULL arrays, n_chunks outside [1, CAKV_MAX_CHUNKS], rank outside
+ * [0, n_chunks), chunk_len < 0.
+ */
+cakv_status cakv_schedule(int rank, int n_chunks, int64_t chunk_len, int causal,
+                          int32_t* blocks_host, int8_t* class_host);
+
+/*
+ * Empty running state for B*Hq*Tq rows: m = -inf, l = 0, o = 0.
+ * m, l: [B, Hq, Tq] fp32; o: [B, Tq, Hq, D] fp32.
+ */
+cakv_status cakv_state_init(float* m, float* l, float* o, int B, int Hq, int Tq, int D,
+                            void* stream);
+
+/*
+ * One ring step: fold one key/value block into the running state (page
+ * section "But softmax seems to require all attention scores at once").
+ * q: [B, Tq, Hq, D] queries at global positions q_offset + row;
+ * k, v: [B, Tkv, Hkv, D] keys/values at global positions kv_offset + row;
+ * dtype: CAKV_BF16 or CAKV_F32 (q, k, v share it); scale <= 0 -> 1/sqrt(D).
+ * m, l, o: running state, read and written in place.
+ * tile_counters (nullable, device int64[2]): the call ADDS the number of
+ * (CAKV_TILE_Q rows x CAKV_TILE_K keys) tiles, per batch row and query head,
+ * that it computed unmasked [0] and masked [1]; tiles of CAKV_SKIP class are
+ * not computed and not counted. A block with no allowed pair (CAKV_SKIP)
+ * returns CAKV_OK and launches nothing.
+ */
+cakv_status cakv_block_update(const void* q, const void* k, const void* v, int dtype,
+                              int B, int Hq, int Hkv, int Tq, int Tkv, int D,
+                              int64_t q_offset, int64_t kv_offset, int causal, float scale,
+                              float* m, float* l, float* o, int64_t* tile_counters,
+                              void* stream);
+
+/*
+ * out = o / l (fp32, or bf16 if out_dtype == CAKV_BF16) and lse = m + ln(l)
+ * (fp32); rows with l == 0 give out = 0, lse = -inf. out may alias o when
+ * out_dtype is CAKV_F32. lse may be NULL.
+ */
+cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* out,
+                          int out_dtype, float* lse, int B, int Hq, int Tq, int D,
+                          void* stream);
+
+/*
+ * Combine two normalised partials of the same rows over disjoint key sets:
+ *   M = max(lse_a, lse_b), lse = M + ln(e^{lse_a-M} + e^{lse_b-M}),
+ *   o = e^{lse_a-lse} o_a + e^{lse_b-lse} o_b; both -inf gives (0, -inf).
+ * o_*: [B, Tq, Hq, D] fp32; lse_*: [B, Hq, Tq] fp32. o_out / lse_out may
+ * alias either input. Page section "Training and inference stress this
+ * dimension differently" (partial results are combined), with the rescale
+ * rule of section "But softmax seems to require all attention scores at
+ * once".
+ */
+cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_b,
+                           const float* lse_b, float* o_out, float* lse_out, int B, int Hq,
+                           int Tq, int D, void* stream);
+
+/*
+ * One rank's whole share: attention of the stationary local queries q_local
+ * (chunk `rank`, global positions rank*chunk_len + row) against the
+ * n_chunks key/value blocks, consumed in ring order rank, rank-1, ...
+ * (cakv_schedule), SKIP blocks never read, then finalised. The running state
+ * stays on chip for the whole ring; nothing but out and lse is written.
+ * q_local: [B, chunk_len, Hq, D];
+ * k_blocks_host, v_blocks_host: HOST arrays of n_chunks device pointers,
+ *   block j = [B, chunk_len, Hkv, D] holding positions [j*chunk_len, ...);
+ * out: [B, chunk_len, Hq, D] in out_dtype; lse: [B, Hq, chunk_len] fp32
+ *   (nullable); tile_counters: as for cakv_block_update (nullable).
+ * Errors: as above plus rank outside [0, n_chunks), n_chunks outside
+ * [1, CAKV_MAX_CHUNKS], a NULL block pointer that the schedule would read.
+ */
+cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_blocks_host,
+                                     const void* const* v_blocks_host, int dtype, int B,
+                                     int Hq, int Hkv, int chunk_len, int n_chunks, int D,
+                                     int rank, int causal, float scale, void* out,
+                                     int out_dtype, float* lse, int64_t* tile_counters,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAKV_H */
