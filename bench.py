@@ -74,6 +74,20 @@ def traffic_for(workload_name: str):
     return rec.get("bytes_per_launch")
 
 
+def calibrate_copy(nbytes: int):
+    """One device copy of nbytes (read nbytes, write nbytes): the reference
+    the FETCH_SIZE / WRITE_SIZE counters of the forward kernel are scaled by."""
+    import torch
+    torch.cuda.set_device(0)
+    n = nbytes // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,7 +98,13 @@ def main():
                     help="target wall time of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device-to-device copy of BYTES bytes (the "
+                         "known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
