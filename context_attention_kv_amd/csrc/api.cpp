@@ -38,12 +38,12 @@ cakv_status hip_status(int err, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Tuning override for the bf16 kernel: query rows per wave (32 or 64).
-int rows_per_wave() {
+// Tuning override for the bf16 kernel: waves per workgroup (4 or 8).
+int bf16_waves() {
     static const int v = [] {
-        const char* e = std::getenv("CAKV_ROWS_PER_WAVE");
-        if (e && std::atoi(e) == 64) return 64;
-        return 32;
+        const char* e = std::getenv("CAKV_WAVES");
+        if (e && std::atoi(e) == 4) return 4;
+        return 8;
     }();
     return v;
 }
@@ -77,10 +77,10 @@ float resolve_scale(float scale, int D) {
 void set_grid(cakv::FwdArgs& a, int dtype, int D) {
     (void)D;
     if (dtype == CAKV_BF16) {
-        const int rw = rows_per_wave();
+        const int nw = bf16_waves();
         const int G = a.Hq / a.Hkv;
-        const long long npblk = (a.Tq + rw - 1) / rw;
-        a.wg_per_bg = (int)((G * npblk + 3) / 4);
+        const long long npblk = (a.Tq + 31) / 32;   // 32 query rows per wave
+        a.wg_per_bg = (int)((G * npblk + nw - 1) / nw);
         a.n_wg = (int)((long long)a.B * a.Hkv * a.wg_per_bg);
     } else {
         const int rows = cakv::fwd_f32_wg_rows();
@@ -90,7 +90,7 @@ void set_grid(cakv::FwdArgs& a, int dtype, int D) {
 }
 
 int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
-    if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, rows_per_wave(), stream);
+    if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, bf16_waves(), stream);
     return cakv::launch_fwd_f32(a, D, stream);
 }
 
