@@ -38,16 +38,6 @@ cakv_status hip_status(int err, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Tuning override for the bf16 kernel: waves per workgroup (4 or 8).
-int bf16_waves() {
-    static const int v = [] {
-        const char* e = std::getenv("CAKV_WAVES");
-        if (e && std::atoi(e) == 4) return 4;
-        return 8;
-    }();
-    return v;
-}
-
 cakv_class classify(int64_t q_off, int64_t q_len, int64_t kv_off, int64_t kv_len, int causal) {
     if (q_len <= 0 || kv_len <= 0) return CAKV_SKIP;
     if (!causal) return CAKV_FULL;
@@ -77,7 +67,7 @@ float resolve_scale(float scale, int D) {
 void set_grid(cakv::FwdArgs& a, int dtype, int D) {
     (void)D;
     if (dtype == CAKV_BF16) {
-        const int nw = bf16_waves();
+        const int nw = cakv::fwd_bf16_waves();
         const int G = a.Hq / a.Hkv;
         const long long npblk = (a.Tq + 31) / 32;   // 32 query rows per wave
         a.wg_per_bg = (int)((G * npblk + nw - 1) / nw);
@@ -90,7 +80,7 @@ void set_grid(cakv::FwdArgs& a, int dtype, int D) {
 }
 
 int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
-    if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, bf16_waves(), stream);
+    if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, stream);
     return cakv::launch_fwd_f32(a, D, stream);
 }
 

@@ -36,9 +36,9 @@ struct FwdArgs {
 };
 
 // Launchers (return the hipError_t of the launch as int).
-int launch_fwd_bf16(const FwdArgs& a, int D, int waves, void* stream);
+int launch_fwd_bf16(const FwdArgs& a, int D, void* stream);
 int launch_fwd_f32(const FwdArgs& a, int D, void* stream);
-int fwd_bf16_wg_rows(int waves);   // query rows (head x position) per workgroup
+int fwd_bf16_waves();   // waves per workgroup (32 query rows each)
 int fwd_f32_wg_rows();
 
 int launch_state_init(float* m, float* l, float* o, long long rows, int D, void* stream);

@@ -9,16 +9,18 @@
 // positions only where a tile straddles the diagonal.
 //
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, 4 SIMDs per CU, 64-wide waves):
-//   * a workgroup is NW waves serving one (batch, kv head); each wave owns 32
+//   * a workgroup is 8 waves serving one (batch, kv head); each wave owns 32
 //     query rows of one query head. With grouped heads the waves take
 //     different query heads of the same positions, so a key/value tile staged
-//     once in LDS feeds every head that reads it. With 8 waves two waves share
-//     each SIMD and the hardware overlaps one wave's softmax ALU work with the
-//     other's matrix instructions.
+//     once in LDS feeds every head that reads it.
+//   * two waves share each SIMD, one from each group of four (waves 0-3 and
+//     4-7), and the groups run one phase apart: while one group does its
+//     matrix phase (P V of the previous tile, then Q K^T of this tile) the
+//     other does its softmax phase, so the SIMD's matrix core and vector ALU
+//     work at the same time. A workgroup barrier separates the phases.
 //   * K and V tiles (64 keys) go from HBM straight into LDS with
-//     global_load_lds_dwordx4 (no staging registers), double-buffered: the
-//     next tile streams in while the current one is multiplied, with one
-//     barrier per tile.
+//     global_load_lds_dwordx4 (no staging registers) into a ring of 4 tile
+//     buffers; the first group issues each tile two tiles ahead.
 //   * per tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A
 //     operand, Q^T held in registers as the B operand), so a lane owns one
 //     query column and its scores sit in its own registers: the row max/sum
@@ -26,9 +28,9 @@
 //     read in a permuted order so each half-wave holds 16 consecutive keys;
 //     P^T (bf16) then feeds O^T += V^T P^T directly as the B operand, and the
 //     V^T operand comes from the row-major V tile through ds_read_b64_tr_b16.
-//   * LDS tiles are XOR-swizzled (16-byte units for K, 32-byte units for V)
-//     so the operand reads are free of bank conflicts; the swizzle is applied
-//     by choosing which global chunk each lane fetches.
+//   * LDS tiles are XOR-swizzled in 16-byte units so the operand reads are
+//     free of bank conflicts; the swizzle is applied by choosing which global
+//     chunk each lane fetches.
 //   * workgroup ids are remapped so that each XCD works through a contiguous
 //     range of (batch, kv head) pairs (their K/V stream then hits that XCD's
 //     L2), heaviest query tiles first.
@@ -61,13 +63,24 @@ constexpr float kLn2 = 0.69314718055994531f;
 __device__ __forceinline__ int key_of_row(int i) {
     return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 }
-// K tile: 16-byte unit c of key row `key` sits at unit c ^ kswz(key). The 8
-// lanes of one ds_read_b128 phase hold keys that differ in bits 0, 1 and 4.
-__device__ __forceinline__ int kswz(int key) { return (key & 3) | ((key >> 2) & 4); }
-// V tile: 16-byte unit u of key row `key` sits at unit u ^ vswz(key): 32-byte
-// units rotate with key % 4, so the four rows one 16-lane group of a
-// transposing read touches fall in four different 32-byte bank ranges.
-__device__ __forceinline__ int vswz(int key) { return 2 * (key & 3); }
+// LDS swizzles: 16-byte unit c of key row `key` of a K tile sits at unit
+// c ^ kswz(key), of a V tile at c ^ vswz(key). They are chosen so that every
+// operand read is free of bank conflicts whether the LDS serves a 16-byte
+// read 8 lanes per cycle over 32 banks or 16 lanes per cycle over 64 banks
+// (and an 8-byte read 16 or 32 lanes per cycle): in one cycle the K reads
+// touch keys that differ in bits 0, 1, 2, 4, the transposing V reads touch
+// four consecutive keys (bits 0, 1) at 2 or 4 adjacent units.
+template <int D>
+__device__ __forceinline__ int kswz(int key) {
+    if constexpr (D == 128)
+        return (key & 3) | (((key >> 4) & 1) << 2) | (((key >> 2) & 1) << 3);
+    else
+        return ((key >> 1) & 1) | (((key >> 4) & 1) << 1) | (((key ^ (key >> 2)) & 1) << 2);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int key) {
+    return (D == 128 ? 11 : 3) * (key & 1) + 4 * ((key >> 1) & 1);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -85,39 +98,62 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int NW>
+template <int D>
 struct Cfg {
+    static constexpr int NW = 8;                   // waves: two groups of four
+    static constexpr int NB = 4;                   // tile buffers in the LDS ring
     static constexpr int DSTEPS = D / 16;          // k-steps of S^T
     static constexpr int DB = D / 32;              // 32-row blocks of O^T
     static constexpr int ROW_BYTES = D * 2;        // one key row of a tile
-    static constexpr int TILE_BYTES = kBK * ROW_BYTES;
+    static constexpr int TILE_BYTES = kBK * ROW_BYTES;     // one K or one V tile
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES;       // K tile, then V tile
     static constexpr int UNITS = D / 8;            // 16-byte units per row
     static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;   // rows one wave load fills
     static constexpr int REGIONS = kBK / ROWS_PER_KB;      // 1 KB regions per tile
-    static constexpr int LOADS = REGIONS / NW;             // per wave, per tensor
-    static_assert(REGIONS % NW == 0, "tile regions must split over the waves");
+    static constexpr int LOADS = REGIONS / 4;              // copies per wave per tile
 };
 
-// Issue the direct-to-LDS loads of one K and one V tile (keys key0..key0+63
-// of a block; rows past kv_len re-read the last key, which the mask drops).
-template <int D, int NW>
-__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ kg,
-                                           const __bf16* __restrict__ vg, long long rs,
-                                           int key0, int kv_len, char* kdst, char* vdst,
-                                           int wave, int lane) {
-    using C = Cfg<D, NW>;
+// One global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at LDS
+// address lds_base + 16 i. Issued as inline assembly so that the compiler does
+// not treat the copy as a pending LDS write to wait for before every later
+// LDS read: completion is awaited explicitly (wait_vmem) before the
+// workgroup barrier that publishes the tile. Vector-memory loads retire in
+// issue order, so these extra loads only make the compiler's own waits
+// stricter, never weaker.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, unsigned lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(gptr), "s"(lds_base)
+        : "memory", "m0");
+}
+
+// Issue this wave's share of the direct-to-LDS copy of one K tile (first
+// group, is_v = false) or one V tile (second group, is_v = true): keys
+// key0..key0+63 of a block, swizzled; rows past kv_len re-read the last key,
+// which the mask drops. `wl` is the wave's index within its group and `dst`
+// the LDS address of the tile.
+template <int D>
+__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ src, bool is_v,
+                                           long long rs, int key0, int kv_len, unsigned dst,
+                                           int wl, int lane) {
+    using C = Cfg<D>;
 #pragma unroll
     for (int n = 0; n < C::LOADS; ++n) {
-        const int region = n * NW + wave;
+        const int region = n * 4 + wl;
         const int row = region * C::ROWS_PER_KB + lane / C::UNITS;
         const int p = lane % C::UNITS;
         const int gk = min(key0 + row, kv_len - 1);
-        const long long roff = (long long)gk * rs;
-        __builtin_amdgcn_global_load_lds(kg + roff + 8 * (p ^ kswz(row)),
-                                         (lds_void*)(kdst + region * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vg + roff + 8 * (p ^ vswz(row)),
-                                         (lds_void*)(vdst + region * 1024), 16, 0, 0);
+        const int sw = is_v ? vswz<D>(row) : kswz<D>(row);
+        copy16_to_lds(src + (long long)gk * rs + 8 * (p ^ sw), dst + region * 1024);
     }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Number of keys of a block this workgroup must look at: all of them, or
@@ -129,17 +165,66 @@ __device__ __forceinline__ int keys_needed(const FwdArgs& a, int t, long long la
     return n <= 0 ? 0 : (n < len ? (int)n : len);
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW)
+// Position in the tile sequence: block (in ring order) and 64-key tile in
+// it, with that block's numbers cached so that stepping costs no loads.
+struct Cursor {
+    int bi, ti;
+    int need, len;          // keys needed / present in block bi
+    long long off;          // global position of the block's key 0
+    const __bf16* kp;       // block bi's K and V at row 0 of (batch b, kv head g)
+    const __bf16* vp;
+};
+// (batch, kv head) coordinates of the workgroup, for the block pointers
+struct HeadAt {
+    int b, g;
+    long long rs;           // key row stride (elements) = Hkv * D
+    int D;
+    long long last;         // last query position of the workgroup
+};
+__device__ __forceinline__ void cursor_load(const FwdArgs& a, const HeadAt& at, Cursor& c) {
+    for (; c.bi < a.n_blocks; ++c.bi) {
+        c.need = keys_needed(a, c.bi, at.last);
+        if (c.need > 0) {
+            c.len = a.kv_len[c.bi];
+            c.off = a.kv_off[c.bi];
+            const long long base = (long long)at.b * c.len * at.rs + (long long)at.g * at.D;
+            c.kp = static_cast<const __bf16*>(a.k[c.bi]) + base;
+            c.vp = static_cast<const __bf16*>(a.v[c.bi]) + base;
+            return;
+        }
+    }
+    c.need = 0;
+}
+__device__ __forceinline__ Cursor cursor_first(const FwdArgs& a, const HeadAt& at) {
+    Cursor c;
+    c.bi = 0;
+    c.ti = 0;
+    cursor_load(a, at, c);
+    return c;
+}
+__device__ __forceinline__ void cursor_next(const FwdArgs& a, const HeadAt& at, Cursor& c) {
+    if (++c.ti * kBK >= c.need) {
+        c.ti = 0;
+        ++c.bi;
+        cursor_load(a, at, c);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(512)
 fwd_bf16_kernel(const FwdArgs a) {
-    using C = Cfg<D, NW>;
+    using C = Cfg<D>;
+    constexpr int NW = C::NW;
     constexpr int RW = 32;
-    // [buffer][K | V][64 keys][D] bf16
-    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * C::TILE_BYTES];
+    // ring of NB buffers: [K tile | V tile], each [64 keys][D] bf16, swizzled
+    __shared__ __attribute__((aligned(1024))) char smem[C::NB * C::BUF_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int l32 = lane & 31, hh = lane >> 5;
+    const bool loader = wave < 4;       // first group: issues the tile loads
+    const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;   // LDS address of the ring
 
     // ---- workgroup -> (batch, kv head, query tile); XCD-contiguous order ----
     const int bid = blockIdx.x;
@@ -215,82 +300,153 @@ fwd_bf16_kernel(const FwdArgs a) {
 
     // ---- lane-constant LDS offsets of the operand reads ----
     // K (A operand of S^T): key 32kb + key_of_row(l32), 16-byte unit 2st + hh;
-    // the K swizzle of that key does not depend on kb.
+    // the K swizzle of that key does not depend on kb (bit 5).
     const int k_row = key_of_row(l32) * C::ROW_BYTES;
-    const int kx = kswz(key_of_row(l32));
+    const int kx = kswz<D>(key_of_row(l32));
     // V^T (A operand of O^T) through the transposing read: in each 16-lane
     // group g16, source lane 4k + q points at key (base + k) and dims
     // 16*(g16 % 2) + 4q .. +3 of the 32-dim block; the group then receives
     // 4 consecutive keys of one dim per lane. Key bases are multiples of 4,
-    // so key % 4 == k and the V swizzle of the row is vswz(k).
+    // so key % 4 == k and the V swizzle (a function of key % 4) is vswz(k).
     const int g16 = lane >> 4, src = lane & 15;
     const int v_key = 16 * (g16 >> 1) + (src >> 2);     // + 32kb + 8j (+4 for items 4..7)
     const int v_dim = 16 * (g16 & 1) + 4 * (src & 3);    // + 32db
-    const int v_sw = vswz(src >> 2);
+    const int v_sw = vswz<D>(src >> 2);
 
+    // The Q (and state) loads above are predicated; wait for them here, in a
+    // form the compiler's wait tracking understands, so that no wait for them
+    // lands inside the loop (where it would also wait for the tile copies).
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     unsigned long long n_full = 0, n_masked = 0;
 
-    // ---- walk the blocks in the given (ring) order, 64 keys at a time ----
-    int bi = 0;
-    while (bi < a.n_blocks && keys_needed(a, bi, wg_last_pos) == 0) ++bi;
-    int ti = 0, buf = 0;
-    if (bi < a.n_blocks) {
-        const long long base = ((long long)b * a.kv_len[bi]) * kv_rs + (long long)g * D;
-        issue_tile<D, NW>(static_cast<const __bf16*>(a.k[bi]) + base,
-                          static_cast<const __bf16*>(a.v[bi]) + base, kv_rs, 0, a.kv_len[bi],
-                          smem, smem + C::TILE_BYTES, wave, lane);
-    }
-    while (bi < a.n_blocks) {
-        const int need = keys_needed(a, bi, wg_last_pos);
-        const int key0 = ti * kBK;
-        int nbi = bi, nti = ti + 1;
-        if (nti * kBK >= need) {
-            nti = 0;
-            ++nbi;
-            while (nbi < a.n_blocks && keys_needed(a, nbi, wg_last_pos) == 0) ++nbi;
-        }
-        // This wave's loads of the current tile are complete; after the
-        // barrier every wave's are, and every wave is done reading the other
-        // buffer, which the next tile's loads may now overwrite.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (nbi < a.n_blocks) {
-            const long long base = ((long long)b * a.kv_len[nbi]) * kv_rs + (long long)g * D;
-            char* nk = smem + (buf ^ 1) * 2 * C::TILE_BYTES;
-            issue_tile<D, NW>(static_cast<const __bf16*>(a.k[nbi]) + base,
-                              static_cast<const __bf16*>(a.v[nbi]) + base, kv_rs, nti * kBK,
-                              a.kv_len[nbi], nk, nk + C::TILE_BYTES, wave, lane);
-        }
-        const lds_char* kt = (const lds_char*)(smem + buf * 2 * C::TILE_BYTES);
-        const lds_char* vt = kt + C::TILE_BYTES;
+    // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
+    const HeadAt at{b, g, kv_rs, D, wg_last_pos};
+    int T = 0;
+    for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
 
-        const int kv_len = a.kv_len[bi];
-        const long long kpos0 = a.kv_off[bi] + key0;
-        const int tile_keys = min(kBK, kv_len - key0);
-        const long long kpos_last = kpos0 + tile_keys - 1;
-        const bool compute = wave_valid && !(a.causal && kpos0 > wave_last_pos);
-        if (compute) {
-            if (!a.causal || kpos_last <= wave_first_pos) ++n_full;
-            else ++n_masked;
-            const bool need_mask = (a.causal && kpos_last > wave_first_pos) || tile_keys < kBK;
+    // Tile copies: the first group copies K tiles, the second V tiles, each
+    // two tiles ahead, into a ring of NB buffers [K | V].
+    const bool copies_v = !loader;
+    const int wl = wave & 3;
+    Cursor ld = cursor_first(a, at);   // next tile this wave copies its share of
+    auto issue = [&](unsigned buf_base) {
+        const unsigned dst = buf_base + (copies_v ? C::TILE_BYTES : 0);
+        const __bf16* src = copies_v ? ld.vp : ld.kp;
+        const int key0 = ld.ti * kBK;
+        if (key0 + kBK <= ld.len) {
+            const __bf16* tile = src + (long long)key0 * kv_rs;
+#pragma unroll
+            for (int n = 0; n < C::LOADS; ++n) {
+                const int region = n * 4 + wl;
+                const int row = region * C::ROWS_PER_KB + lane / C::UNITS;
+                const int p = lane % C::UNITS;
+                const int sw = copies_v ? vswz<D>(row) : kswz<D>(row);
+                copy16_to_lds(tile + row * kv_rs + 8 * (p ^ sw), dst + region * 1024);
+            }
+        } else {
+            issue_tile<D>(src, copies_v, kv_rs, key0, ld.len, dst, wl, lane);
+        }
+        cursor_next(a, at, ld);
+    };
+    if (T > 0) issue(lds0);
+    if (T > 1) issue(lds0 + C::BUF_BYTES);
+    if (T > 1) wait_vmem<C::LOADS>();
+    else wait_vmem<0>();
+    __syncthreads();
+    if (!loader) __syncthreads();   // the second group runs one phase behind
 
-            // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
-            f32x16 s[2];
+    // V^T fragment i of a tile (i = (kb, j, db), db fastest) and K fragment i
+    // (i = (st, kb), kb fastest); both are A operands of 32x32x16 products.
+    auto v_frag = [&](const lds_char* vt, int i) -> u32x4 {
+        const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
+        const int key = 32 * kb + 8 * j + v_key;
+        const int d = 32 * db + v_dim;
+        const int off = key * C::ROW_BYTES + 16 * ((d >> 3) ^ v_sw) + 2 * (d & 7);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + off + 4 * C::ROW_BYTES));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    auto k_frag = [&](const lds_char* kt, int i) -> u32x4 {
+        const int st = i / 2, kb = i % 2;
+        return *(const lds_u32x4*)(kt + kb * 32 * C::ROW_BYTES + k_row + 16 * ((2 * st + hh) ^ kx));
+    };
+    constexpr int NPV = 4 * C::DB;       // P V products per tile
+    constexpr int NQK = 2 * C::DSTEPS;   // Q K^T products per tile
+
+    Cursor cq = cursor_first(a, at);   // tile of this wave's Q K^T
+    bool have_p = false;       // P of the previous tile is waiting for its P V
+    u32x4 pb[2][2];            // P^T of the previous tile (bf16), B operand of P V
+    for (int t = 0; t <= T; ++t) {
+        // ================= matrix phase: P V (tile t-1), Q K^T (tile t) =================
+        const lds_char* vt = (const lds_char*)(smem + ((t + C::NB - 1) % C::NB) * C::BUF_BYTES +
+                                               C::TILE_BYTES);
+        const lds_char* kt = (const lds_char*)(smem + (t % C::NB) * C::BUF_BYTES);
+        bool cmp = false;
+        long long kpos0 = 0;
+        int tile_keys = 0;
+        bool need_mask = false;
+        if (t < T) {
+            const int key0 = cq.ti * kBK;
+            kpos0 = cq.off + key0;
+            tile_keys = min(kBK, cq.len - key0);
+            const long long kpos_last = kpos0 + tile_keys - 1;
+            cmp = wave_valid && !(a.causal && kpos0 > wave_last_pos);
+            if (cmp) {
+                if (!a.causal || kpos_last <= wave_first_pos) ++n_full;
+                else ++n_masked;
+                need_mask = (a.causal && kpos_last > wave_first_pos) || tile_keys < kBK;
+            }
+        }
+        if (have_p) {
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+                const u32x4 vf = v_frag(vt, i);
+                const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
+                o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(vf), as_bf16x8(pb[kb][j]), o_acc[db], 0, 0, 0);
+            }
+            // pipeline: reads of 4 fragments ahead, then one MFMA per fragment
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < NPV - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
+        f32x16 s[2];
+        if (cmp) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-            for (int st = 0; st < C::DSTEPS; ++st) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 kf = *(const lds_u32x4*)(kt + kb * 32 * C::ROW_BYTES + k_row +
-                                                         16 * ((2 * st + hh) ^ kx));
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf),
-                                                                    as_bf16x8(qf[st]), s[kb], 0, 0, 0);
-                }
+            for (int i = 0; i < NQK; ++i) {
+                const u32x4 kf = k_frag(kt, i);
+                s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(kf), as_bf16x8(qf[i / 2]), s[i % 2], 0, 0, 0);
             }
+            // pipeline: 4 fragment reads ahead, then one MFMA per read
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NQK - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+        __syncthreads();
+        if (t == T) break;
 
+        // ================= softmax phase (tile t) =================
+        // This group starts its share of the copy of tile t+2 into the buffer
+        // of tile t-2, which no wave reads any more (see the phase schedule).
+        if (t + 2 < T) issue(lds0 + ((t + 2) % C::NB) * C::BUF_BYTES);
+        if (cmp) {
             // scores as plain floats; the mask keeps r <= lim of each 16-key run
             float sv[2][16];
 #pragma unroll
@@ -311,7 +467,6 @@ fwd_bf16_kernel(const FwdArgs a) {
                     for (int r = 0; r < 16; ++r) sv[kb][r] = r <= lm ? sv[kb][r] : -INFINITY;
                 }
             }
-
             // online softmax (log2 domain: t = score * scale * log2 e)
             float mx = -INFINITY;
 #pragma unroll
@@ -322,7 +477,6 @@ fwd_bf16_kernel(const FwdArgs a) {
             const float m_new = fmaxf(m_run, mx * a.scale_log2);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2(m_run - m_use);
-            u32x4 pb[2][2];
             float rs = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -330,9 +484,9 @@ fwd_bf16_kernel(const FwdArgs a) {
                 for (int j = 0; j < 2; ++j) {
                     f32x8 p;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        p[t] = fast_exp2(__builtin_fmaf(sv[kb][8 * j + t], a.scale_log2, -m_use));
-                        rs += p[t];
+                    for (int u = 0; u < 8; ++u) {
+                        p[u] = fast_exp2(__builtin_fmaf(sv[kb][8 * j + u], a.scale_log2, -m_use));
+                        rs += p[u];
                     }
                     pb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
                 }
@@ -344,31 +498,17 @@ fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) o_acc[db] *= alpha;
             }
-
-            // O^T += V^T P^T; V^T fragments through transposing LDS reads
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        const int key = 32 * kb + 8 * j + v_key;
-                        const int d = 32 * db + v_dim;
-                        const int off = key * C::ROW_BYTES + 16 * ((d >> 3) ^ v_sw) + 2 * (d & 7);
-                        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
-                        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4*)(vt + off + 4 * C::ROW_BYTES));
-                        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-                        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-                        const u32x4 vf = {l2[0], l2[1], h2[0], h2[1]};
-                        o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(vf), as_bf16x8(pb[kb][j]), o_acc[db], 0, 0, 0);
-                    }
         }
-        bi = nbi;
-        ti = nti;
-        buf ^= 1;
+        have_p = cmp;
+        cursor_next(a, at, cq);
+        // this wave's share of tile t+1 must have landed before the barrier
+        // that opens the phase reading it; the copies of tile t+2 may still
+        // be in flight
+        if (t + 2 < T) wait_vmem<C::LOADS>();
+        else wait_vmem<0>();
+        __syncthreads();
     }
+    if (loader) __syncthreads();    // match the second group's extra barrier
 
     // ---- epilogue: store state, or finalise into out / lse ----
     if (wave_valid) {
@@ -420,20 +560,20 @@ fwd_bf16_kernel(const FwdArgs a) {
     }
 }
 
-template <int D, int NW>
+template <int D>
 int launch(const FwdArgs& a, void* stream) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW>), dim3(a.n_wg), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
                        static_cast<hipStream_t>(stream), a);
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int fwd_bf16_wg_rows(int waves) { return waves * 32; }
+int fwd_bf16_waves() { return 8; }
 
-int launch_fwd_bf16(const FwdArgs& a, int D, int waves, void* stream) {
-    if (D == 128) return waves == 4 ? launch<128, 4>(a, stream) : launch<128, 8>(a, stream);
-    if (D == 64) return waves == 4 ? launch<64, 4>(a, stream) : launch<64, 8>(a, stream);
+int launch_fwd_bf16(const FwdArgs& a, int D, void* stream) {
+    if (D == 128) return launch<128>(a, stream);
+    if (D == 64) return launch<64>(a, stream);
     return (int)hipErrorInvalidValue;
 }
 
