@@ -48,6 +48,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -113,42 +115,34 @@ struct Cfg {
     static constexpr int LOADS = REGIONS / 4;              // copies per wave per tile
 };
 
-// One global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at LDS
-// address lds_base + 16 i. Issued as inline assembly so that the compiler does
-// not treat the copy as a pending LDS write to wait for before every later
-// LDS read: completion is awaited explicitly (wait_vmem) before the
-// workgroup barrier that publishes the tile. Vector-memory loads retire in
-// issue order, so these extra loads only make the compiler's own waits
-// stricter, never weaker.
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, unsigned lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
-        :
-        : "v"(gptr), "s"(lds_base)
-        : "memory", "m0");
+// Buffer resource of `bytes` bytes at `base` (raw: stride 0, 32-bit data
+// format). Lanes whose offset falls at or past `bytes` read nothing: the
+// range check returns zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+    i32x4 r;
+    r[0] = (int)(unsigned)a;
+    r[1] = (int)((a >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
 }
 
-// Issue this wave's share of the direct-to-LDS copy of one K tile (first
-// group, is_v = false) or one V tile (second group, is_v = true): keys
-// key0..key0+63 of a block, swizzled; rows past kv_len re-read the last key,
-// which the mask drops. `wl` is the wave's index within its group and `dst`
-// the LDS address of the tile.
-template <int D>
-__device__ __forceinline__ void issue_tile(const __bf16* __restrict__ src, bool is_v,
-                                           long long rs, int key0, int kv_len, unsigned dst,
-                                           int wl, int lane) {
-    using C = Cfg<D>;
-#pragma unroll
-    for (int n = 0; n < C::LOADS; ++n) {
-        const int region = n * 4 + wl;
-        const int row = region * C::ROWS_PER_KB + lane / C::UNITS;
-        const int p = lane % C::UNITS;
-        const int gk = min(key0 + row, kv_len - 1);
-        const int sw = is_v ? vswz<D>(row) : kswz<D>(row);
-        copy16_to_lds(src + (long long)gk * rs + 8 * (p ^ sw), dst + region * 1024);
-    }
+// One buffer -> LDS copy of 16 bytes per lane: lane i's 16 bytes, from byte
+// offset voff of the resource, land at LDS address lds_base + 16 i. Issued as
+// inline assembly so that the compiler does not treat the copy as a pending
+// LDS write to wait for before every later LDS read: completion is awaited
+// explicitly (wait_vmem) before the workgroup barrier that publishes the
+// tile. Vector-memory loads retire in issue order, so these extra loads only
+// make the compiler's own waits stricter, never weaker.
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds_base)
+        : "memory", "m0");
 }
 
 template <int N>
@@ -329,23 +323,32 @@ fwd_bf16_kernel(const FwdArgs a) {
     const bool copies_v = !loader;
     const int wl = wave & 3;
     Cursor ld = cursor_first(a, at);   // next tile this wave copies its share of
-    auto issue = [&](unsigned buf_base) {
-        const unsigned dst = buf_base + (copies_v ? C::TILE_BYTES : 0);
-        const __bf16* src = copies_v ? ld.vp : ld.kp;
-        const int key0 = ld.ti * kBK;
-        if (key0 + kBK <= ld.len) {
-            const __bf16* tile = src + (long long)key0 * kv_rs;
+    // Lane-constant parts of the copies: copy n fills 1 KB region n*4 + wl of
+    // the K (first group) or V (second group) tile; this lane fetches the
+    // 16-byte unit p of key row `row` of the tile, swizzled (byte offset).
+    unsigned cp_off[C::LOADS];
 #pragma unroll
-            for (int n = 0; n < C::LOADS; ++n) {
-                const int region = n * 4 + wl;
-                const int row = region * C::ROWS_PER_KB + lane / C::UNITS;
-                const int p = lane % C::UNITS;
-                const int sw = copies_v ? vswz<D>(row) : kswz<D>(row);
-                copy16_to_lds(tile + row * kv_rs + 8 * (p ^ sw), dst + region * 1024);
-            }
-        } else {
-            issue_tile<D>(src, copies_v, kv_rs, key0, ld.len, dst, wl, lane);
-        }
+    for (int n = 0; n < C::LOADS; ++n) {
+        const int row = (n * 4 + wl) * C::ROWS_PER_KB + lane / C::UNITS;
+        const int p = lane % C::UNITS;
+        cp_off[n] = (unsigned)(2 * (row * kv_rs + 8 * (p ^ (copies_v ? vswz<D>(row) : kswz<D>(row)))));
+    }
+    // Resource covering the rows of the tile at cursor `ld` that exist in its
+    // block (rows past the block's end read as zeros, which the mask drops),
+    // or nothing.
+    auto tile_rsrc = [&](bool any) -> i32x4 {
+        const int key0 = ld.ti * kBK;
+        const int rows = any ? min(kBK, ld.len - key0) : 0;
+        return make_rsrc((copies_v ? ld.vp : ld.kp) + (long long)key0 * kv_rs,
+                         (unsigned)(rows * kv_rs * 2));
+    };
+    auto copy_part = [&](i32x4 rsrc, unsigned buf, int n) {
+        copy16_to_lds(rsrc, cp_off[n], buf + (copies_v ? C::TILE_BYTES : 0) + (n * 4 + wl) * 1024);
+    };
+    auto issue = [&](unsigned buf) {
+        const i32x4 rsrc = tile_rsrc(true);
+#pragma unroll
+        for (int n = 0; n < C::LOADS; ++n) copy_part(rsrc, buf, n);
         cursor_next(a, at, ld);
     };
     if (T > 0) issue(lds0);
@@ -379,6 +382,8 @@ fwd_bf16_kernel(const FwdArgs a) {
     Cursor cq = cursor_first(a, at);   // tile of this wave's Q K^T
     bool have_p = false;       // P of the previous tile is waiting for its P V
     u32x4 pb[2][2];            // P^T of the previous tile (bf16), B operand of P V
+    constexpr int NPRE = 4;    // V^T fragments of the previous tile read ahead
+    u32x4 vpre[NPRE];
     for (int t = 0; t <= T; ++t) {
         // ================= matrix phase: P V (tile t-1), Q K^T (tile t) =================
         const lds_char* vt = (const lds_char*)(smem + ((t + C::NB - 1) % C::NB) * C::BUF_BYTES +
@@ -400,22 +405,33 @@ fwd_bf16_kernel(const FwdArgs a) {
                 need_mask = (a.causal && kpos_last > wave_first_pos) || tile_keys < kBK;
             }
         }
+        // the matrix phase issues first on the SIMD it shares with the other
+        // group's softmax phase, so that its products follow each other
+        __builtin_amdgcn_s_setprio(1);
+        // the first K fragments of Q K^T are read before P V, which hides
+        // their latency behind the P V products
+        u32x4 kpre[NPRE];
+        if (cmp) {
+#pragma unroll
+            for (int i = 0; i < NPRE; ++i) kpre[i] = k_frag(kt, i);
+        }
         if (have_p) {
 #pragma unroll
             for (int i = 0; i < NPV; ++i) {
-                const u32x4 vf = v_frag(vt, i);
+                const u32x4 vf = i < NPRE ? vpre[i] : v_frag(vt, i);
                 const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
                 o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(vf), as_bf16x8(pb[kb][j]), o_acc[db], 0, 0, 0);
             }
-            // pipeline: reads of 4 fragments ahead, then one MFMA per fragment
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            // pipeline: the first NPRE fragments were read in the softmax
+            // phase; each product is followed by the reads of the fragment
+            // NPRE ahead
 #pragma unroll
-            for (int i = 0; i < NPV - 4; ++i) {
+            for (int i = 0; i < NPV - NPRE; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
         }
         // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
         f32x16 s[2];
@@ -426,45 +442,58 @@ fwd_bf16_kernel(const FwdArgs a) {
                 for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
-                const u32x4 kf = k_frag(kt, i);
+                const u32x4 kf = i < NPRE ? kpre[i] : k_frag(kt, i);
                 s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(kf), as_bf16x8(qf[i / 2]), s[i % 2], 0, 0, 0);
             }
-            // pipeline: 4 fragment reads ahead, then one MFMA per read
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            // pipeline: one MFMA, then the read of the fragment NPRE ahead
 #pragma unroll
-            for (int i = 0; i < NQK - 4; ++i) {
+            for (int i = 0; i < NQK - NPRE; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
         if (t == T) break;
 
         // ================= softmax phase (tile t) =================
-        // This group starts its share of the copy of tile t+2 into the buffer
-        // of tile t-2, which no wave reads any more (see the phase schedule).
-        if (t + 2 < T) issue(lds0 + ((t + 2) % C::NB) * C::BUF_BYTES);
+        // This group copies its share of tile t+2 into the buffer of tile t-2,
+        // which no wave reads any more (see the phase schedule). The copies
+        // are spread over the phase, one per quarter of the exponentials, so
+        // that the address units take them while the vector ALU works. In
+        // the last two phases there is no tile t+2 and the copies read
+        // nothing.
+        const unsigned cbuf = lds0 + ((t + 2) % C::NB) * C::BUF_BYTES;
+        const i32x4 crsrc = tile_rsrc(t + 2 < T);
+        auto copy_at = [&](int n) {
+            if (n < C::LOADS) copy_part(crsrc, cbuf, n);
+            __builtin_amdgcn_sched_barrier(0);
+        };
         if (cmp) {
-            // scores as plain floats; the mask keeps r <= lim of each 16-key run
-            float sv[2][16];
+            // the first V^T fragments of this tile for the next phase's P V
+            // (its V tile was published two phases ago)
+            {
+                const lds_char* vcur = (const lds_char*)(smem + (t % C::NB) * C::BUF_BYTES +
+                                                         C::TILE_BYTES);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sv[kb][r] = s[kb][r];
+                for (int i = 0; i < NPRE; ++i) vpre[i] = v_frag(vcur, i);
+            }
             if (need_mask) {
+                // keep key r of each 16-key run where r <= lim
+                // query minus key position at key 0 of the tile, clamped into
+                // 32 bits (beyond +-2^30 the causal limit no longer binds)
+                const long long dq64 = qpos - kpos0;
+                const int dq = dq64 > (1 << 30) ? (1 << 30) : (dq64 < -(1 << 30) ? -(1 << 30) : (int)dq64);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int run0 = 32 * kb + 16 * hh;
-                    long long lim = tile_keys - 1 - run0;
-                    if (a.causal) {
-                        const long long lc = qpos - (kpos0 + run0);
-                        lim = lc < lim ? lc : lim;
-                    }
-                    const int lm = lim < -1 ? -1 : (lim > 15 ? 15 : (int)lim);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sv[kb][r] = r <= lm ? sv[kb][r] : -INFINITY;
+                    int lim = tile_keys - 1 - run0;
+                    if (a.causal) lim = min(lim, dq - run0);
+                    const i32x16 ridx = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
+                    const f32x16 ninf = -INFINITY;
+                    s[kb] = ridx <= lim ? s[kb] : ninf;
                 }
             }
             // online softmax (log2 domain: t = score * scale * log2 e)
@@ -472,33 +501,40 @@ fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[kb][r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = half_max(mx);
             const float m_new = fmaxf(m_run, mx * a.scale_log2);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2(m_run - m_use);
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x8 p;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        p[u] = fast_exp2(__builtin_fmaf(sv[kb][8 * j + u], a.scale_log2, -m_use));
-                        rs += p[u];
-                    }
-                    pb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
-                }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
             // rescale O only when some row's maximum moved (wave-uniform test;
             // rows whose maximum did not move have alpha = 1)
             if (__any(alpha != 1.f)) {
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) o_acc[db] *= alpha;
             }
+            float rs = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    copy_at(2 * kb + j);
+                    f32x8 p;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        p[u] = fast_exp2(__builtin_fmaf(s[kb][8 * j + u], a.scale_log2, -m_use));
+                        rs += p[u];
+                    }
+                    pb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
+                }
+#pragma unroll
+            for (int n = 4; n < C::LOADS; ++n) copy_at(n);
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+        } else {
+#pragma unroll
+            for (int n = 0; n < C::LOADS; ++n) copy_at(n);
         }
+        if (t + 2 < T) cursor_next(a, at, ld);
         have_p = cmp;
         cursor_next(a, at, cq);
         // this wave's share of tile t+1 must have landed before the barrier
