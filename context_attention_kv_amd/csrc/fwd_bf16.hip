@@ -167,6 +167,11 @@ struct Cursor {
     long long off;          // global position of the block's key 0
     const __bf16* kp;       // block bi's K and V at row 0 of (batch b, kv head g)
     const __bf16* vp;
+    // block bi against the rows of this wave: rel = position of its key 0
+    // minus the wave's first query position, clamped into 32 bits (only
+    // read when the block is neither wholly before nor wholly after them)
+    bool all_full;          // every key at or before the wave's first row (or no mask)
+    int rel;
 };
 // (batch, kv head) coordinates of the workgroup, for the block pointers
 struct HeadAt {
@@ -174,6 +179,8 @@ struct HeadAt {
     long long rs;           // key row stride (elements) = Hkv * D
     int D;
     long long last;         // last query position of the workgroup
+    long long wfirst;       // first query position of this wave
+    int causal;
 };
 __device__ __forceinline__ void cursor_load(const FwdArgs& a, const HeadAt& at, Cursor& c) {
     for (; c.bi < a.n_blocks; ++c.bi) {
@@ -184,6 +191,9 @@ __device__ __forceinline__ void cursor_load(const FwdArgs& a, const HeadAt& at, 
             const long long base = (long long)at.b * c.len * at.rs + (long long)at.g * at.D;
             c.kp = static_cast<const __bf16*>(a.k[c.bi]) + base;
             c.vp = static_cast<const __bf16*>(a.v[c.bi]) + base;
+            c.all_full = !at.causal || c.off + c.len - 1 <= at.wfirst;
+            const long long rel = c.off - at.wfirst;
+            c.rel = c.all_full ? 0 : (rel > (1 << 30) ? (1 << 30) : (int)rel);
             return;
         }
     }
@@ -204,7 +214,8 @@ __device__ __forceinline__ void cursor_next(const FwdArgs& a, const HeadAt& at, 
     }
 }
 
-template <int D>
+// COUNT: tally the tiles each wave computes (full / masked) into a.counters
+template <int D, bool COUNT>
 __global__ void __launch_bounds__(512)
 fwd_bf16_kernel(const FwdArgs a) {
     using C = Cfg<D>;
@@ -242,8 +253,6 @@ fwd_bf16_kernel(const FwdArgs a) {
     const long long wg_last_pos = a.q_off + wg_last_row;
     const int wave_rows = wave_valid ? min(RW, a.Tq - row0) : 0;
     const long long wave_first_pos = a.q_off + row0;
-    const long long wave_last_pos = a.q_off + row0 + wave_rows - 1;
-    const long long qpos = a.q_off + row0 + l32;      // this lane's query position
 
     const long long q_rs = (long long)a.Hq * D;
     const long long kv_rs = (long long)a.Hkv * D;
@@ -311,10 +320,10 @@ fwd_bf16_kernel(const FwdArgs a) {
     // form the compiler's wait tracking understands, so that no wait for them
     // lands inside the loop (where it would also wait for the tile copies).
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    unsigned long long n_full = 0, n_masked = 0;
+    unsigned n_full = 0, n_masked = 0;   // tiles this wave computed, unmasked / masked
 
     // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
-    const HeadAt at{b, g, kv_rs, D, wg_last_pos};
+    const HeadAt at{b, g, kv_rs, D, wg_last_pos, wave_first_pos, a.causal};
     int T = 0;
     for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
 
@@ -389,32 +398,14 @@ fwd_bf16_kernel(const FwdArgs a) {
         const lds_char* vt = (const lds_char*)(smem + ((t + C::NB - 1) % C::NB) * C::BUF_BYTES +
                                                C::TILE_BYTES);
         const lds_char* kt = (const lds_char*)(smem + (t % C::NB) * C::BUF_BYTES);
-        bool cmp = false;
-        long long kpos0 = 0;
-        int tile_keys = 0;
-        bool need_mask = false;
-        if (t < T) {
-            const int key0 = cq.ti * kBK;
-            kpos0 = cq.off + key0;
-            tile_keys = min(kBK, cq.len - key0);
-            const long long kpos_last = kpos0 + tile_keys - 1;
-            cmp = wave_valid && !(a.causal && kpos0 > wave_last_pos);
-            if (cmp) {
-                if (!a.causal || kpos_last <= wave_first_pos) ++n_full;
-                else ++n_masked;
-                need_mask = (a.causal && kpos_last > wave_first_pos) || tile_keys < kBK;
-            }
-        }
         // the matrix phase issues first on the SIMD it shares with the other
         // group's softmax phase, so that its products follow each other
         __builtin_amdgcn_s_setprio(1);
         // the first K fragments of Q K^T are read before P V, which hides
         // their latency behind the P V products
         u32x4 kpre[NPRE];
-        if (cmp) {
 #pragma unroll
-            for (int i = 0; i < NPRE; ++i) kpre[i] = k_frag(kt, i);
-        }
+        for (int i = 0; i < NPRE; ++i) kpre[i] = k_frag(kt, i);
         if (have_p) {
 #pragma unroll
             for (int i = 0; i < NPV; ++i) {
@@ -433,9 +424,12 @@ fwd_bf16_kernel(const FwdArgs a) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
         }
-        // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
+        // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r).
+        // Computed for every tile (and once past the last one, on a stale
+        // but finite buffer) so that no branch delays the products; the
+        // softmax phase drops the scores of tiles this wave skips.
         f32x16 s[2];
-        if (cmp) {
+        {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -453,6 +447,21 @@ fwd_bf16_kernel(const FwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, NPRE, 0);
+        }
+        // tile t against this wave's rows (scalar work, after the products
+        // are issued): k0r = position of the tile's key 0 minus the wave's
+        // first query position
+        // (branch-free; past the last tile the cursor's numbers are stale
+        // and only cmp = false matters)
+        const int key0 = cq.ti * kBK;
+        const int tile_keys = min(kBK, cq.len - key0);
+        const int k0r = cq.all_full ? -(1 << 30) : min(cq.rel, kBK) + key0;
+        const bool full = k0r + tile_keys - 1 <= 0;
+        const bool cmp = t < T && wave_valid && k0r <= wave_rows - 1;
+        const bool need_mask = !full || tile_keys < kBK;
+        if constexpr (COUNT) {
+            n_full += cmp && full ? 1u : 0u;
+            n_masked += cmp && !full ? 1u : 0u;
         }
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
@@ -482,10 +491,8 @@ fwd_bf16_kernel(const FwdArgs a) {
             }
             if (need_mask) {
                 // keep key r of each 16-key run where r <= lim
-                // query minus key position at key 0 of the tile, clamped into
-                // 32 bits (beyond +-2^30 the causal limit no longer binds)
-                const long long dq64 = qpos - kpos0;
-                const int dq = dq64 > (1 << 30) ? (1 << 30) : (dq64 < -(1 << 30) ? -(1 << 30) : (int)dq64);
+                // query minus key position at key 0 of the tile
+                const int dq = l32 - k0r;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int run0 = 32 * kb + 16 * hh;
@@ -590,16 +597,20 @@ fwd_bf16_kernel(const FwdArgs a) {
             }
         }
     }
-    if (a.counters && lane == 0 && (n_full | n_masked)) {
-        atomicAdd(a.counters + 0, n_full);
-        atomicAdd(a.counters + 1, n_masked);
+    if (COUNT && lane == 0 && (n_full | n_masked)) {
+        atomicAdd(a.counters + 0, (unsigned long long)n_full);
+        atomicAdd(a.counters + 1, (unsigned long long)n_masked);
     }
 }
 
 template <int D>
 int launch(const FwdArgs& a, void* stream) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
-                       static_cast<hipStream_t>(stream), a);
+    if (a.counters)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
+                           static_cast<hipStream_t>(stream), a);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
+                           static_cast<hipStream_t>(stream), a);
     return (int)hipGetLastError();
 }
 
