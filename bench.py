@@ -14,7 +14,10 @@ Printed: ONE JSON line. value = useful TFLOP/s (4 d_k FLOPs per allowed
 (query, key) pair, masked work not counted) over the timed steps; roofline =
 the forward kernel's useful FLOPs per launch over its HIP-event-timed launch
 duration against the bf16 dense matrix peak (256 CUs x 2.4 GHz x 4096
-FLOP/clk = 2516.6 TFLOP/s); cpu_baseline = the fp64 CPU oracle timed on a
+FLOP/clk = 2516.6 TFLOP/s), plus roofline.sustained_mfma: the rate the
+matrix cores hold on this chip with back-to-back bf16 products from registers
+(random and zero operands; the clock settles lower for random ones) and
+frac_of_sustained = achieved / the random-operand rate; cpu_baseline = the fp64 CPU oracle timed on a
 bounded row sample on this host's cores (its rows double as a parity spot
 check, reported under "parity"); kernels = the bandwidth-bound finalize and
 log-sum-exp merge kernels timed at this workload's row count against 8 TB/s.
@@ -35,6 +38,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12      # 2516.58
 PEAK_F32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+CEILING_ITERS = 200000   # ~0.35-0.5 s per cakv_diag_mfma_burn launch
 METRIC = "local-shard attention TFLOP/s (useful causal FLOPs), % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "fwd_bf16.hip")
@@ -98,6 +102,8 @@ def main():
                     help="target wall time of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the sustained matrix-core rate measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy of BYTES bytes (the "
                          "known-size reference for HBM byte counters) and exit")
@@ -199,6 +205,28 @@ def main():
         "avg_launch_ms": round(sum(launch_ms) / len(launch_ms), 4),
         "flops_per_launch": per_launch[0] if len(set(per_launch)) == 1 else None,
     }
+
+    # ---- what the matrix cores sustain on this chip (bf16 workloads) -------
+    # back-to-back bf16 products from registers on every compute unit: random
+    # operands (the practical ceiling: power draw follows the operand bits and
+    # the clock settles lower) and zeros
+    if is_bf16 and not args.no_ceiling:
+        sink = torch.zeros(4, device="cuda")
+        cakv.cakv_diag_mfma_burn(False, 20000, sink)
+        rates = {}
+        for name, zero in (("random_operands", False), ("zero_operands", True)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cakv.cakv_diag_mfma_burn(zero, CEILING_ITERS, sink)
+            b.record(stream)
+            torch.cuda.synchronize()
+            rates[name] = round(cakv.diag_mfma_flops(CEILING_ITERS) / (a.elapsed_time(b) * 1e-3)
+                                / 1e12, 1)
+        roofline["sustained_mfma"] = dict(rates, unit="TFLOP/s", what=(
+            "bf16 32x32x16 products back to back from registers on every CU "
+            "(cakv_diag_mfma_burn)"))
+        roofline["frac_of_sustained"] = round(achieved / rates["random_operands"], 4)
+        log("matrix-core ceiling measured")
 
     # ---- bandwidth-bound kernels at this workload's row count ---------------
     kernels = {}

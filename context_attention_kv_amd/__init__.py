@@ -29,8 +29,9 @@ CAKV_TILE_Q, CAKV_TILE_K = 32, 64
 EXPORTED = (
     "cakv_abi_version", "cakv_status_str", "cakv_last_error", "cakv_classify_block",
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
-    "cakv_lse_merge", "cakv_local_shard_forward",
+    "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn",
 )
+DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
 
 
 class CakvError(RuntimeError):
@@ -64,6 +65,7 @@ def _load_lib():
         "cakv_finalize": ([P, P, P, P, I, P, I, I, I, I, P], I),
         "cakv_lse_merge": ([P, P, P, P, P, P, I, I, I, I, P], I),
         "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, P], I),
+        "cakv_diag_mfma_burn": ([I, I64, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -200,3 +202,14 @@ def cakv_local_shard_forward(q_local, k_blocks: Sequence, v_blocks: Sequence, ra
                                          _ptr(out), _dtype_code(out), _ptr(lse),
                                          _ptr(tile_counters), _stream(stream)),
            "cakv_local_shard_forward")
+
+
+def cakv_diag_mfma_burn(zero_operands: bool, iters: int, sink, stream=None):
+    """Measurement aid: back-to-back bf16 matrix-core products on every compute
+    unit (random or zero operands); FLOPs = diag_mfma_flops(iters)."""
+    _check(_lib.cakv_diag_mfma_burn(int(bool(zero_operands)), int(iters), _ptr(sink),
+                                    _stream(stream)), "cakv_diag_mfma_burn")
+
+
+def diag_mfma_flops(iters: int) -> float:
+    return float(DIAG_MFMA_WG) * 4 * iters * 16 * 32768

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "cakv.h"
+#include "cakv_diag.h"
 #include "fwd_args.h"
 
 namespace {
@@ -264,6 +265,15 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     set_grid(a, dtype, D);
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
+}
+
+cakv_status cakv_diag_mfma_burn(int zero_operands, int64_t iters, float* sink, void* stream) {
+    if (iters < 0 || iters > 2147483647LL)
+        return fail(CAKV_ERR_SHAPE, "iters=%lld outside [0, 2^31)", (long long)iters);
+    if (iters == 0) return ok();
+    if (!sink) return fail(CAKV_ERR_NULL, "sink is NULL");
+    return hip_status(cakv::launch_mfma_burn(zero_operands != 0, (int)iters, sink, stream),
+                      "mfma_burn launch");
 }
 
 }  // extern "C"

@@ -42,6 +42,7 @@ int fwd_bf16_waves();   // waves per workgroup (32 query rows each)
 int fwd_f32_wg_rows();
 
 int launch_state_init(float* m, float* l, float* o, long long rows, int D, void* stream);
+int launch_mfma_burn(int zero, int iters, float* sink, void* stream);
 int launch_finalize(const float* m, const float* l, const float* o, void* out, int out_bf16,
                     float* lse, int B, int Hq, int Tq, int D, void* stream);
 int launch_lse_merge(const float* o_a, const float* lse_a, const float* o_b,

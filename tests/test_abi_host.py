@@ -1,6 +1,6 @@
 """Host-only checks of the C ABI (no GPU needed; nothing here launches work).
 
-* libcakv.so loads and exports every function include/cakv.h declares.
+* libcakv.so loads and exports every function include/*.h declares.
 * cakv_schedule reproduces the ring rounds printed on the web page "Sequence
   parallelism -- splitting the token dimension across GPUs" (section "A better
   mental model: move blocks past the queries") and, bit for bit, the block
@@ -23,9 +23,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _header_functions():
-    text = open(os.path.join(ROOT, "include", "cakv.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cakv_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(cakv_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported():
@@ -184,3 +188,10 @@ def test_state_finalize_merge_errors():
     assert L.cakv_lse_merge(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 1, 1, 64, None) == 1
     assert L.cakv_lse_merge(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 48, None) == 2
     assert L.cakv_lse_merge(FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 1, 1, 1, 64, None) == 4
+
+
+def test_diag_mfma_burn_errors():
+    assert L.cakv_diag_mfma_burn(0, -1, FAKE, None) == 2
+    assert L.cakv_diag_mfma_burn(0, 1 << 31, FAKE, None) == 2
+    assert L.cakv_diag_mfma_burn(0, 5, None, None) == 1
+    assert L.cakv_diag_mfma_burn(0, 0, None, None) == 0   # nothing to launch

@@ -249,3 +249,13 @@ def test_empty_problems_are_noops():
     out = torch.empty((0, 8, 2, 64), dtype=torch.float32, device="cuda")
     cakv.cakv_local_shard_forward(x, [x], [x], 0, True, out)
     torch.cuda.synchronize()
+
+
+def test_diag_mfma_burn_runs():
+    """The chip-ceiling measurement aid launches and leaves its sink alone."""
+    sink = torch.zeros(4, device="cuda")
+    for zero in (False, True):
+        cakv.cakv_diag_mfma_burn(zero, 8, sink)
+    torch.cuda.synchronize()
+    assert float(sink[0]) == 0.0
+    assert cakv.diag_mfma_flops(8) == 2048 * 4 * 8 * 16 * 32768
