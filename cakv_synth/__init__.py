@@ -210,3 +210,56 @@ def sample_rows(w: Workload, per_head: int, seed: int = 0, fixed=True) -> np.nda
 def scaled(w: Workload, **kw) -> Workload:
     """A copy of `w` with some fields replaced (smaller test variants)."""
     return dataclasses.replace(w, **kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Decode over a KV history held in portions: a sequence of `hist` history
+    tokens followed by Tn new tokens. The history is cut into N equal portions;
+    the new tokens' own keys and values are appended to the last portion (they
+    are in the cache when the new queries run, under the causal rule)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    hist: int
+    N: int
+    Tn: int
+    D: int
+    causal: bool = True
+    v_dist: int = NORMAL
+    seed: int = 0
+
+    @property
+    def total(self) -> int:
+        return self.hist + self.Tn
+
+    def portions(self):
+        """(offset, length) of each portion, in position order."""
+        P = self.hist // self.N
+        out = [(j * P, P) for j in range(self.N)]
+        o, l = out[-1]
+        out[-1] = (o, self.total - o)
+        return out
+
+
+DECODE_WORKLOADS = {
+    1: DecodeWorkload("decode-small-B2-Hq8-Hkv2-hist1000-N4-Tn4-d128", B=2, Hq=8, Hkv=2,
+                      hist=1000, N=4, Tn=4, D=128, seed=2001),
+    2: DecodeWorkload("decode-million-token-hist1048576-N8-Hq32-Hkv8-Tn1-d128-bf16", B=1, Hq=32,
+                      Hkv=8, hist=1048576, N=8, Tn=1, D=128, v_dist=UNIFORM, seed=2002),
+}
+
+
+def make_decode(w: DecodeWorkload):
+    """(q [B, Tn, Hq, D], k [B, total, Hkv, D], v) as bf16 bits: the Tn new
+    queries are rows hist .. hist+Tn-1 of the sequence's Q stream, k and v the
+    whole sequence's K and V streams."""
+    q = np.empty((w.B, w.Tn, w.Hq, w.D), np.uint16)
+    for b in range(w.B):
+        fill(q[b], seed=w.seed, tensor=TENSOR_Q, n0=((b * w.total + w.hist) * w.Hq) * w.D)
+    k = np.empty((w.B, w.total, w.Hkv, w.D), np.uint16)
+    v = np.empty((w.B, w.total, w.Hkv, w.D), np.uint16)
+    fill(k, seed=w.seed, tensor=TENSOR_K)
+    fill(v, seed=w.seed, tensor=TENSOR_V, dist=w.v_dist)
+    return q, k, v

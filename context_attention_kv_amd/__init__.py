@@ -29,7 +29,8 @@ CAKV_TILE_Q, CAKV_TILE_K = 32, 64
 EXPORTED = (
     "cakv_abi_version", "cakv_status_str", "cakv_last_error", "cakv_classify_block",
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
-    "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn",
+    "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
+    "cakv_decode_workspace_size",
 )
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
 
@@ -66,6 +67,8 @@ def _load_lib():
         "cakv_lse_merge": ([P, P, P, P, P, P, I, I, I, I, P], I),
         "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, P], I),
         "cakv_diag_mfma_burn": ([I, I64, P, P], I),
+        "cakv_decode": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P], I),
+        "cakv_decode_workspace_size": ([I, I, I, I, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -213,3 +216,47 @@ def cakv_diag_mfma_burn(zero_operands: bool, iters: int, sink, stream=None):
 
 def diag_mfma_flops(iters: int) -> float:
     return float(DIAG_MFMA_WG) * 4 * iters * 16 * 32768
+
+
+def cakv_decode_workspace_size(B: int, Hq: int, Hkv: int, Tn: int, D: int,
+                               kv_lens: Sequence[int]) -> int:
+    """Bytes of workspace cakv_decode needs for these sizes."""
+    n = len(kv_lens)
+    lens = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_lens])
+    out = ctypes.c_int64(0)
+    _check(_lib.cakv_decode_workspace_size(B, Hq, Hkv, Tn, D, lens, n, ctypes.byref(out)),
+           "cakv_decode_workspace_size")
+    return out.value
+
+
+def cakv_decode(q, k_portions: Sequence, v_portions: Sequence, kv_offsets: Sequence[int],
+                q_offset: int, causal: bool, out, lse=None, workspace=None, scale: float = 0.0,
+                stream=None):
+    """New queries q [B, Tn, Hq, D] (positions q_offset ...) against KV history
+    portions k/v [B, L_j, Hkv, D] at global offsets kv_offsets[j]; writes out
+    [B, Tn, Hq, D] and lse [B, Hq, Tn]. workspace: a device tensor of at least
+    cakv_decode_workspace_size bytes (allocated here when None)."""
+    _contig(q, out, lse, *k_portions, *v_portions)
+    B, Tn, Hq, D = q.shape
+    n = len(k_portions)
+    if len(v_portions) != n or len(kv_offsets) != n or n == 0:
+        raise ValueError("need the same positive number of K portions, V portions and offsets")
+    Hkv = k_portions[0].shape[2]
+    lens = []
+    for kp, vp in zip(k_portions, v_portions):
+        if kp.shape != vp.shape or kp.shape[0] != B or kp.shape[2] != Hkv or kp.shape[3] != D:
+            raise ValueError("every portion must be [B, L_j, Hkv, D] for K and V alike")
+        lens.append(int(kp.shape[1]))
+    if workspace is None:
+        import torch
+        nbytes = cakv_decode_workspace_size(B, Hq, Hkv, Tn, D, lens)
+        workspace = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    karr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in k_portions])
+    varr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in v_portions])
+    larr = (ctypes.c_int64 * n)(*lens)
+    oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
+    _check(_lib.cakv_decode(_ptr(q), karr, varr, larr, oarr, n, _dtype_code(q), B, Hq, Hkv, Tn,
+                            D, int(q_offset), int(causal), float(scale), _ptr(out),
+                            _dtype_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                            _stream(stream)), "cakv_decode")

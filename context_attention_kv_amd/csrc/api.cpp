@@ -2,6 +2,7 @@
 // launch of the kernels. Declarations, layouts and error rules: include/cakv.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 
 #include "cakv.h"
 #include "cakv_diag.h"
+#include "decode_args.h"
 #include "fwd_args.h"
 
 namespace {
@@ -83,6 +85,49 @@ void set_grid(cakv::FwdArgs& a, int dtype, int D) {
 int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
     if (dtype == CAKV_BF16) return cakv::launch_fwd_bf16(a, D, stream);
     return cakv::launch_fwd_f32(a, D, stream);
+}
+
+// Decode plan: how many splits the history's 64-key tiles are cut into.
+// About 4096 waves in flight over the chip (two 64 KB-LDS waves fit a CU at
+// d=128), each split at least one tile.
+struct DecodePlan {
+    int nrb;               // 32-row blocks per (batch, kv head)
+    long long tiles;       // tiles of all portions
+    int tiles_per_split;
+    int n_splits;
+    long long ws_bytes;    // m, l, o of every split's rows
+};
+
+cakv_status decode_plan(int B, int Hq, int Hkv, int Tn, int D, const int64_t* kv_len,
+                        int n_portions, DecodePlan* p) {
+    if (B < 0 || Tn < 0) return fail(CAKV_ERR_SHAPE, "negative size (B=%d Tn=%d)", B, Tn);
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+        return fail(CAKV_ERR_SHAPE, "heads must be positive with Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
+                    Hq, Hkv);
+    if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    if (n_portions < 1 || n_portions > CAKV_MAX_CHUNKS)
+        return fail(CAKV_ERR_RANGE, "n_portions=%d outside [1, %d]", n_portions, CAKV_MAX_CHUNKS);
+    if (!kv_len) return fail(CAKV_ERR_NULL, "kv_len_host is NULL");
+    long long tiles = 0;
+    for (int j = 0; j < n_portions; ++j) {
+        if (kv_len[j] < 0 || kv_len[j] > 2147483647LL - cakv::kDecTile)
+            return fail(CAKV_ERR_SHAPE, "portion %d length %lld out of range", j, (long long)kv_len[j]);
+        tiles += (kv_len[j] + cakv::kDecTile - 1) / cakv::kDecTile;
+    }
+    if (tiles > 2147483647LL) return fail(CAKV_ERR_SHAPE, "too many key tiles (%lld)", tiles);
+    const long long R = (long long)(Hq / Hkv) * Tn;
+    p->nrb = (int)((R + 31) / 32);
+    p->tiles = tiles;
+    const long long per_split = std::max(1LL, (long long)B * Hkv * p->nrb);
+    long long want = std::max(1LL, (4096 + per_split - 1) / per_split);
+    want = std::min(want, std::max(1LL, tiles));
+    const long long tps = std::max(1LL, (tiles + want - 1) / want);
+    p->tiles_per_split = (int)tps;
+    p->n_splits = (int)std::max(1LL, (tiles + tps - 1) / tps);
+    p->ws_bytes = (long long)p->n_splits * per_split * 32 * (D + 2) * 4;
+    if ((long long)p->n_splits * per_split > 2147483647LL)
+        return fail(CAKV_ERR_SHAPE, "decode grid too large");
+    return CAKV_OK;
 }
 
 }  // namespace
@@ -265,6 +310,83 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     set_grid(a, dtype, D);
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
+}
+
+cakv_status cakv_decode_workspace_size(int B, int Hq, int Hkv, int Tn, int D,
+                                       const int64_t* kv_len_host, int n_portions,
+                                       int64_t* bytes_host) {
+    if (!bytes_host) return fail(CAKV_ERR_NULL, "bytes_host is NULL");
+    DecodePlan p;
+    const cakv_status s = decode_plan(B, Hq, Hkv, Tn, D, kv_len_host, n_portions, &p);
+    if (s != CAKV_OK) return s;
+    *bytes_host = (B == 0 || Tn == 0) ? 0 : p.ws_bytes;
+    return ok();
+}
+
+cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
+                        const void* const* v_portions_host, const int64_t* kv_len_host,
+                        const int64_t* kv_off_host, int n_portions, int dtype, int B, int Hq,
+                        int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
+                        int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+    if (dtype != CAKV_BF16 && dtype != CAKV_F32)
+        return fail(CAKV_ERR_DTYPE, "dtype %d is neither CAKV_F32 nor CAKV_BF16", dtype);
+    if (dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "cakv_decode takes bf16 inputs only");
+    if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
+    DecodePlan p;
+    cakv_status s = decode_plan(B, Hq, Hkv, Tn, D, kv_len_host, n_portions, &p);
+    if (s != CAKV_OK) return s;
+    if (B == 0 || Tn == 0) return ok();
+    if (!q || !out) return fail(CAKV_ERR_NULL, "q or out is NULL");
+    if (!k_portions_host || !v_portions_host || !kv_off_host)
+        return fail(CAKV_ERR_NULL, "portion pointer / offset array is NULL");
+    if (!workspace) return fail(CAKV_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < p.ws_bytes)
+        return fail(CAKV_ERR_SHAPE, "workspace of %lld bytes, %lld needed",
+                    (long long)workspace_bytes, p.ws_bytes);
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+        return fail(CAKV_ERR_ALIGN, "q/out/workspace not 16-byte aligned");
+
+    cakv::DecArgs a;
+    std::memset(&a, 0, sizeof a);
+    int tile = 0;
+    for (int j = 0; j < n_portions; ++j) {
+        a.tile0[j] = tile;
+        a.kv_len[j] = (int)kv_len_host[j];
+        a.kv_off[j] = kv_off_host[j];
+        if (kv_len_host[j] > 0) {
+            const void* kp = k_portions_host[j];
+            const void* vp = v_portions_host[j];
+            if (!kp || !vp) return fail(CAKV_ERR_NULL, "portion %d pointer is NULL", j);
+            if (!aligned16(kp) || !aligned16(vp))
+                return fail(CAKV_ERR_ALIGN, "portion %d not 16-byte aligned", j);
+            a.k[j] = kp;
+            a.v[j] = vp;
+        }
+        tile += (int)((kv_len_host[j] + cakv::kDecTile - 1) / cakv::kDecTile);
+    }
+    a.tile0[n_portions] = tile;
+    a.n_portions = n_portions;
+    a.q = q;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tn = Tn;
+    a.q_off = q_off;
+    a.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    a.causal = causal ? 1 : 0;
+    a.nrb = p.nrb;
+    a.tiles_per_split = p.tiles_per_split;
+    a.n_splits = p.n_splits;
+    const long long rows = (long long)p.n_splits * B * Hkv * p.nrb * 32;
+    a.ws_m = static_cast<float*>(workspace);
+    a.ws_l = a.ws_m + rows;
+    a.ws_o = a.ws_l + rows + ((4 - (2 * rows) % 4) % 4);   // 16-byte aligned rows
+    a.out = out;
+    a.out_bf16 = out_dtype == CAKV_BF16;
+    a.lse = lse;
+    s = hip_status(cakv::launch_decode_split(a, D, stream), "decode split launch");
+    if (s != CAKV_OK) return s;
+    return hip_status(cakv::launch_decode_merge(a, D, stream), "decode merge launch");
 }
 
 cakv_status cakv_diag_mfma_burn(int zero_operands, int64_t iters, float* sink, void* stream) {

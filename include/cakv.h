@@ -194,6 +194,55 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
                                      int out_dtype, float* lse, int64_t* tile_counters,
                                      void* stream);
 
+/*
+ * Decode over a KV history held in portions (page section "Training and
+ * inference stress this dimension differently": during inference each device
+ * holds one portion of a long conversation's keys and values, the new query
+ * is evaluated against every portion and the partial attention results are
+ * combined). On one GPU the portions are device buffers; the call reads each
+ * once, cut into many splits processed side by side, and merges the splits'
+ * online-softmax states with the log-sum-exp rule (the rescale rule of
+ * section "But softmax seems to require all attention scores at once").
+ * Called with one portion it yields that portion's normalised partial
+ * (out_j, lse_j); cakv_lse_merge combines such partials of disjoint portions.
+ *
+ * q: [B, Tn, Hq, D] bf16, the Tn new queries at global positions
+ *   q_off .. q_off + Tn - 1;
+ * k_portions_host, v_portions_host: HOST arrays of n_portions device
+ *   pointers, portion j = [B, kv_len_host[j], Hkv, D] bf16 whose key 0 sits at
+ *   global position kv_off_host[j] (HOST int64 arrays); portions may come in
+ *   any order and need not be adjacent; an empty portion's pointers may be
+ *   NULL. causal != 0 hides keys at positions after a query's own (the new
+ *   tokens' keys may be part of the last portion); every history key before
+ *   q_off is visible either way.
+ * out: [B, Tn, Hq, D] in out_dtype; lse: [B, Hq, Tn] fp32 natural log
+ *   (nullable). A row that sees no key gets out = 0, lse = -inf.
+ * workspace: device buffer of at least cakv_decode_workspace_size bytes for
+ *   the splits' states, 16-byte aligned, owned by the caller; its contents
+ *   are scratch. Calls that share a workspace must not overlap in time.
+ * Errors: CAKV_ERR_DTYPE unless dtype = CAKV_BF16 (fp32 decode is not
+ * provided) or for an unknown out_dtype; CAKV_ERR_SHAPE for sizes as in
+ * cakv_block_update, a portion length outside [0, 2^31 - 64] or a workspace
+ * that is too small; CAKV_ERR_RANGE for n_portions outside
+ * [1, CAKV_MAX_CHUNKS]; CAKV_ERR_NULL / CAKV_ERR_ALIGN as usual. B = 0 or
+ * Tn = 0 returns CAKV_OK and launches nothing.
+ */
+cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
+                        const void* const* v_portions_host, const int64_t* kv_len_host,
+                        const int64_t* kv_off_host, int n_portions, int dtype, int B, int Hq,
+                        int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
+                        int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Bytes of workspace cakv_decode needs for these sizes (written to the HOST
+ * int64 *bytes_host; 0 when B or Tn is 0). Same argument checks as
+ * cakv_decode.
+ */
+cakv_status cakv_decode_workspace_size(int B, int Hq, int Hkv, int Tn, int D,
+                                       const int64_t* kv_len_host, int n_portions,
+                                       int64_t* bytes_host);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,3 +195,39 @@ def test_diag_mfma_burn_errors():
     assert L.cakv_diag_mfma_burn(0, 1 << 31, FAKE, None) == 2
     assert L.cakv_diag_mfma_burn(0, 5, None, None) == 1
     assert L.cakv_diag_mfma_burn(0, 0, None, None) == 0   # nothing to launch
+
+
+def test_decode_errors_and_workspace_size():
+    I64 = ctypes.c_int64
+    lens = (I64 * 3)(1000, 0, 64)
+    offs = (I64 * 3)(0, 1000, 1000)
+    ptrs = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+    nb = I64(0)
+    # workspace size: 17 tiles; (B=1, Hkv=2, one 32-row block) -> splits of one tile
+    assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, lens, 3, ctypes.byref(nb)) == 0
+    assert nb.value == 17 * 1 * 2 * 1 * 32 * (128 + 2) * 4
+    assert L.cakv_decode_workspace_size(0, 8, 2, 4, 128, lens, 3, ctypes.byref(nb)) == 0
+    assert nb.value == 0
+    assert L.cakv_decode_workspace_size(1, 8, 3, 4, 128, lens, 3, ctypes.byref(nb)) == 2
+    assert L.cakv_decode_workspace_size(1, 8, 2, 4, 96, lens, 3, ctypes.byref(nb)) == 2
+    assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, lens, 0, ctypes.byref(nb)) == 5
+    assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, None, 3, ctypes.byref(nb)) == 1
+    bad = (I64 * 1)(-1)
+    assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, bad, 1, ctypes.byref(nb)) == 2
+    need = 17 * 2 * 32 * 130 * 4
+
+    def dec(q=FAKE, k=ptrs, v=ptrs, n=3, dtype=1, B=1, D=128, out=FAKE, odt=0, ws=FAKE,
+            wsb=need):
+        return L.cakv_decode(q, k, v, lens, offs, n, dtype, B, 8, 2, 4, D, 1004, 1, 0.0, out,
+                             odt, None, ws, wsb, None)
+    assert dec(dtype=0) == 3            # fp32 decode is not provided
+    assert dec(dtype=7) == 3
+    assert dec(odt=5) == 3
+    assert dec(n=0) == 5
+    assert dec(D=80) == 2
+    assert dec(q=None) == 1
+    assert dec(ws=None) == 1
+    assert dec(wsb=need - 4) == 2
+    assert dec(q=MIS) == 4
+    assert dec(k=None) == 1
+    assert dec(B=0, q=None, out=None, ws=None) == 0   # nothing to do

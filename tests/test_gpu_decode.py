@@ -1,0 +1,152 @@
+"""GPU parity of decode over a KV history held in portions (web page
+"Sequence parallelism -- splitting the token dimension across GPUs", section
+"Training and inference stress this dimension differently": the new query
+is evaluated against the portions and the partial results are combined).
+
+Every case compares cakv_decode (through the C ABI) with the fp64 oracle on
+the same seeded inputs, to the bf16 tolerances of gpu_util.TOL. The oracle
+side is either one attention over the whole contiguous history or, where the
+portions are shuffled, gapped or empty, one attention per portion combined
+with the oracle's log-sum-exp merge.
+"""
+import numpy as np
+import pytest
+import torch
+
+import cakv_synth as syn
+import context_attention_kv_amd as cakv
+import oracle
+from gpu_util import all_rows, compare, gather_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _portions_dev(k, v, bounds):
+    kd, vd = to_dev(k), to_dev(v)
+    kp = [kd[:, o:o + l].contiguous() for o, l in bounds]
+    vp = [vd[:, o:o + l].contiguous() for o, l in bounds]
+    return kp, vp
+
+
+def _run(qd, kp, vp, offs, q_off, causal, out_dtype=torch.float32):
+    B, Tn, Hq, D = qd.shape
+    out = torch.empty((B, Tn, Hq, D), dtype=out_dtype, device="cuda")
+    lse = torch.empty((B, Hq, Tn), dtype=torch.float32, device="cuda")
+    cakv.cakv_decode(qd, kp, vp, offs, q_off, causal, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _oracle_by_portions(q, k, v, bounds, q_off, causal, rows):
+    """One fp64 attention per portion, combined with the oracle merge."""
+    acc_o, acc_l = None, None
+    for o, l in bounds:
+        if l == 0:
+            continue
+        po, pl = oracle.attention(q, k[:, o:o + l], v[:, o:o + l], q_off=q_off, k_off=o,
+                                  causal=causal, rows=rows)
+        if acc_o is None:
+            acc_o, acc_l = po, pl
+        else:
+            acc_o, acc_l = oracle.lse_merge(acc_o, acc_l, po, pl)
+    return acc_o, acc_l
+
+
+@pytest.mark.parametrize("Tn", [1, 4, 16])
+def test_decode_small_all_rows(Tn):
+    w = syn.scaled(syn.DECODE_WORKLOADS[1], Tn=Tn)
+    q, k, v = syn.make_decode(w)
+    bounds = w.portions()
+    kp, vp = _portions_dev(k, v, bounds)
+    say(f"decode {w.name} Tn={Tn} portions={bounds}")
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], w.hist, True)
+    rows = all_rows(w.B, w.Hq, w.Tn)
+    ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=True, rows=rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", f"decode Tn={Tn}", rows)
+
+
+def test_decode_d64_bidirectional_bf16_out():
+    w = syn.scaled(syn.DECODE_WORKLOADS[1], D=64, Hq=12, Hkv=3, hist=777, N=3, Tn=3,
+                   causal=False, seed=2011)
+    q, k, v = syn.make_decode(w)
+    bounds = w.portions()
+    kp, vp = _portions_dev(k, v, bounds)
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], w.hist, False,
+                    out_dtype=torch.bfloat16)
+    rows = all_rows(w.B, w.Hq, w.Tn)
+    ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=False, rows=rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", "decode d=64 bidirectional, bf16 out", rows)
+
+
+def test_decode_shuffled_gapped_empty_portions():
+    """Portions in any order, not adjacent (a gap of history left out), one
+    empty and one shorter than a tile."""
+    w = syn.scaled(syn.DECODE_WORKLOADS[1], hist=1500, Tn=2, seed=2012)
+    q, k, v = syn.make_decode(w)
+    bounds = [(900, 602), (0, 300), (300, 0), (310, 37), (347, 500)]   # 847..899 left out
+    order = [3, 0, 4, 2, 1]
+    bounds = [bounds[i] for i in order]
+    kp, vp = _portions_dev(k, v, bounds)
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], w.hist, True)
+    rows = all_rows(w.B, w.Hq, w.Tn)
+    ro, rl = _oracle_by_portions(q, k, v, bounds, w.hist, True, rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", "decode shuffled / gapped / empty portions", rows)
+
+
+def test_decode_per_portion_partials_then_merge():
+    """Each portion alone gives its normalised partial (o_j, lse_j); the LSE
+    merge kernel combines them into the same result as one call over all."""
+    w = syn.DECODE_WORKLOADS[1]
+    q, k, v = syn.make_decode(w)
+    bounds = w.portions()
+    kp, vp = _portions_dev(k, v, bounds)
+    qd = to_dev(q)
+    acc_o = acc_l = None
+    for j, (o, _) in enumerate(bounds):
+        po, pl = _run(qd, [kp[j]], [vp[j]], [o], w.hist, True)
+        if acc_o is None:
+            acc_o, acc_l = po, pl
+        else:
+            cakv.cakv_lse_merge(acc_o, acc_l, po, pl, acc_o, acc_l)
+    torch.cuda.synchronize()
+    rows = all_rows(w.B, w.Hq, w.Tn)
+    ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=True, rows=rows)
+    go, gl = gather_rows(acc_o, acc_l, rows)
+    compare(go, gl, ro, rl, "bf16", "per-portion partials + merge", rows)
+    full_o, full_l = _run(qd, kp, vp, [o for o, _ in bounds], w.hist, True)
+    fo, fl = gather_rows(full_o, full_l, rows)
+    assert np.abs(fo - go).max() <= 1e-3 and np.abs(fl - gl).max() <= 1e-4
+
+
+def test_decode_rows_without_keys_and_noops():
+    """All keys after the queries (causal): out = 0, lse = -inf. B = 0 and
+    Tn = 0 launch nothing."""
+    w = syn.scaled(syn.DECODE_WORKLOADS[1], hist=256, Tn=2, seed=2013)
+    q, k, v = syn.make_decode(w)
+    kp, vp = _portions_dev(k, v, [(0, 256)])
+    out, lse = _run(to_dev(q), kp, vp, [10_000], 0, True)   # keys at 10000.. > queries 0, 1
+    assert float(out.abs().max()) == 0.0
+    assert torch.isinf(lse).all() and (lse < 0).all()
+    z = torch.empty((0, 2, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    cakv.cakv_decode(z, [kp[0][:0]], [vp[0][:0]], [0], 0, True,
+                     torch.empty((0, 2, w.Hq, w.D), device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_decode_million_token_history_all_rows():
+    """The benchmarked decode workload at full size: one new token per batch
+    against a 1,048,576-token history in 8 portions (its own key in the last),
+    every query row against the oracle."""
+    w = syn.DECODE_WORKLOADS[2]
+    q, k, v = syn.make_decode(w)
+    bounds = w.portions()
+    kp, vp = _portions_dev(k, v, bounds)
+    say(f"decode {w.name}")
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], w.hist, True)
+    rows = all_rows(w.B, w.Hq, w.Tn)
+    ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=True, rows=rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", "decode million-token history", rows)
