@@ -92,6 +92,82 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
 
 
+def bench_decode(args):
+    """Decode over a KV history in portions (HBM-bound): new tokens per second
+    and algorithmic HBM bytes (the whole history's K and V, the new queries,
+    out and lse) per call over the HIP-event-timed call."""
+    import numpy as np
+    import torch
+
+    import cakv_synth as syn
+    import context_attention_kv_amd as cakv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = syn.DECODE_WORKLOADS[args.decode]
+    log(f"generating {w.name}")
+    q, k, v = syn.make_decode(w)
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    kd = torch.from_numpy(k.view(np.int16)).cuda().view(torch.bfloat16)
+    vd = torch.from_numpy(v.view(np.int16)).cuda().view(torch.bfloat16)
+    del k, v
+    bounds = w.portions()
+    kp = [kd[:, o:o + l].contiguous() for o, l in bounds]
+    vp = [vd[:, o:o + l].contiguous() for o, l in bounds]
+    offs = [o for o, _ in bounds]
+    out = torch.empty((w.B, w.Tn, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Tn), dtype=torch.float32, device="cuda")
+    nbytes = cakv.cakv_decode_workspace_size(w.B, w.Hq, w.Hkv, w.Tn, w.D, [l for _, l in bounds])
+    ws = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        cakv.cakv_decode(qd, kp, vp, offs, w.hist, w.causal, out, lse, workspace=ws)
+
+    steps = max(args.steps, 1) * 10
+    for _ in range(max(args.warmup, 1) * 5):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    kv_bytes = 2 * w.B * w.total * w.Hkv * w.D * 2
+    alg = kv_bytes + w.B * w.Tn * w.Hq * w.D * (2 + 4) + w.B * w.Hq * w.Tn * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "decode over a KV history in portions: algorithmic HBM GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1) * 5,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "history": w.hist,
+                   "portions": w.N, "new_tokens": w.Tn, "d_k": w.D, "causal": w.causal},
+        "new_tokens_per_s": round(w.B * w.Tn / (ms * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_call": alg, "avg_call_ms": round(ms, 4),
+                     "workspace_bytes": nbytes},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,12 +180,18 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained matrix-core rate measurement")
+    ap.add_argument("--decode", type=int, default=0, choices=[0, 1, 2], metavar="CFG",
+                    help="time cakv_decode on decode workload CFG (2 = million-token "
+                         "history) instead of the forward path")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy of BYTES bytes (the "
                          "known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.decode:
+        bench_decode(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -87,8 +87,8 @@ int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
     return cakv::launch_fwd_f32(a, D, stream);
 }
 
-// Decode plan: how many splits the history's 64-key tiles are cut into.
-// About 4096 waves in flight over the chip (two 64 KB-LDS waves fit a CU at
+// Decode plan: how many splits the history's 32-key tiles are cut into.
+// About 4096 waves over the chip (three 48 KB-LDS waves fit a CU at
 // d=128), each split at least one tile.
 struct DecodePlan {
     int nrb;               // 32-row blocks per (batch, kv head)
@@ -123,7 +123,8 @@ cakv_status decode_plan(int B, int Hq, int Hkv, int Tn, int D, const int64_t* kv
     want = std::min(want, std::max(1LL, tiles));
     const long long tps = std::max(1LL, (tiles + want - 1) / want);
     p->tiles_per_split = (int)tps;
-    p->n_splits = (int)std::max(1LL, (tiles + tps - 1) / tps);
+    p->n_splits = (int)std::max(1LL, (tiles + tps - 1) / tps);   // <= 4096 (merge weights in LDS)
+    if (p->n_splits > 4096) return fail(CAKV_ERR_INTERNAL, "decode plan: %d splits", p->n_splits);
     p->ws_bytes = (long long)p->n_splits * per_split * 32 * (D + 2) * 4;
     if ((long long)p->n_splits * per_split > 2147483647LL)
         return fail(CAKV_ERR_SHAPE, "decode grid too large");

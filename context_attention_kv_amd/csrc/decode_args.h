@@ -8,10 +8,10 @@
 
 namespace cakv {
 
-constexpr int kDecTile = 64;   // keys per decode tile
+constexpr int kDecTile = 32;   // keys per decode tile
 
 // New query rows against key/value history portions, split over many waves.
-// The tiles of all portions (64 keys each, a portion's last tile possibly
+// The tiles of all portions (32 keys each, a portion's last tile possibly
 // short) are numbered portion by portion; split s covers tiles
 // [s * tiles_per_split, (s + 1) * tiles_per_split). Wave (s, b, g, rb) folds
 // those tiles into an online-softmax state for row block rb (32 rows) of kv

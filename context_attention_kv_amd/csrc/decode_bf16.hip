@@ -12,16 +12,18 @@
 //
 // decode_split_kernel: one wave per workgroup. Wave (split s, batch b, kv
 // head g, row block rb) owns 32 query rows -- row r = i * G + j is new query i
-// of query head g * G + j, G = Hq / Hkv -- and folds the 64-key tiles of split
+// of query head g * G + j, G = Hq / Hkv -- and folds the 32-key tiles of split
 // s into a running state (m, l, o) exactly as the forward kernel does for one
 // tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as A, Q^T in
 // registers as B), mask from global positions where a tile reaches past a
 // row's position or past its portion's end, online softmax in the log2
-// domain, O^T += V^T P^T with V^T read through ds_read_b64_tr_b16. K and V
-// tiles go from HBM into a double buffer in LDS with buffer_load_dwordx4 ...
-// lds while the wave computes the previous tile.
-// decode_merge_kernel: one wave per row: M = max_s m_s, L = sum_s 2^(m_s-M) l_s,
-// out = sum_s 2^(m_s-M) o_s / L, lse = (M + log2 L) ln 2.
+// domain, O^T += V^T P^T with V^T read through ds_read_b64_tr_b16. Tiles are
+// 32 keys; K and V go from HBM into a ring of three tile buffers in LDS with
+// buffer_load_dwordx4 ... lds, two tiles ahead of the one being computed, so
+// that each wave keeps two tiles of reads in flight (48 KB of LDS per wave
+// at d=128: three waves per CU).
+// decode_merge_kernel: one workgroup per row: M = max_s m_s,
+// L = sum_s 2^(m_s-M) l_s, out = sum_s 2^(m_s-M) o_s / L, lse = (M + log2 L) ln 2.
 #include <hip/hip_runtime.h>
 
 #include "decode_args.h"
@@ -115,6 +117,7 @@ struct DCfg {
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = kDecTile * ROW_BYTES;    // one K or one V tile
     static constexpr int BUF_BYTES = 2 * TILE_BYTES;           // [K | V]
+    static constexpr int NBUF = 3;                             // ring of tile buffers
     static constexpr int UNITS = D / 8;                        // 16-byte units per row
     static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
     static constexpr int REGIONS = kDecTile / ROWS_PER_KB;     // 1 KB copies per K (or V) tile
@@ -132,7 +135,7 @@ __device__ __forceinline__ int xcd_logical(int bid, int n) {
 template <int D>
 __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
     using C = DCfg<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::BUF_BYTES];
     const int lane = threadIdx.x;
     const int l32 = lane & 31, hh = lane >> 5;
     const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
@@ -203,20 +206,19 @@ __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
         while (pj + 1 < a.n_portions && a.tile0[pj + 1] <= t) ++pj;
     };
 
-    // operand reads: K fragment i = (st, kb), V^T fragment i = (kb, j, db)
+    // operand reads: K fragment st, V^T fragment i = (j, db) of the 32-key tile
     const int k_row = key_of_row(l32) * C::ROW_BYTES;
     const int kx = kswz<D>(key_of_row(l32));
     const int g16 = lane >> 4, src = lane & 15;
     const int v_key = 16 * (g16 >> 1) + (src >> 2);
     const int v_dim = 16 * (g16 & 1) + 4 * (src & 3);
     const int v_sw = vswz<D>(src >> 2);
-    auto k_frag = [&](const lds_char* kt, int i) -> u32x4 {
-        const int st = i / 2, kb = i % 2;
-        return *(const lds_u32x4*)(kt + kb * 32 * C::ROW_BYTES + k_row + 16 * ((2 * st + hh) ^ kx));
+    auto k_frag = [&](const lds_char* kt, int st) -> u32x4 {
+        return *(const lds_u32x4*)(kt + k_row + 16 * ((2 * st + hh) ^ kx));
     };
     auto v_frag = [&](const lds_char* vt, int i) -> u32x4 {
-        const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
-        const int key = 32 * kb + 8 * j + v_key;
+        const int db = i % C::DB, j = i / C::DB;
+        const int key = 8 * j + v_key;
         const int d = 32 * db + v_dim;
         const int off = key * C::ROW_BYTES + 16 * ((d >> 3) ^ v_sw) + 2 * (d & 7);
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
@@ -234,56 +236,54 @@ __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
         for (int q = 0; q < 16; ++q) o_acc[db][q] = 0.f;
 
     int tc = t0, pc = p0;   // next tile to copy
-    if (ntiles > 0) {
-        issue_tile(tc, pc, lds0);
-        next_tile(tc, pc);
-    }
-    int tq = t0, pq = p0;   // tile being computed
-    for (int i = 0; i < ntiles; ++i) {
-        const unsigned cur = (i & 1) * C::BUF_BYTES;
-        wait_vmem<0>();   // tile i has landed
-        // the other buffer was read by tile i-1, whose products have
-        // consumed their operands: copy tile i+1 into it now
-        if (i + 1 < ntiles) {
-            issue_tile(tc, pc, lds0 + (cur ^ C::BUF_BYTES));
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        if (k < ntiles) {
+            issue_tile(tc, pc, lds0 + k * C::BUF_BYTES);
             next_tile(tc, pc);
         }
-        const lds_char* kt = (const lds_char*)(smem + cur);
-        const lds_char* vt = (const lds_char*)(smem + cur + C::TILE_BYTES);
+    int tq = t0, pq = p0;   // tile being computed
+    int cur = 0;            // its buffer
+    for (int i = 0; i < ntiles; ++i) {
+        // tile i has landed (tile i+1 may still be in flight)
+        if (i + 1 < ntiles) wait_vmem<2 * C::REGIONS>();
+        else wait_vmem<0>();
+        // the buffer after next held tile i-1, whose products have consumed
+        // their operands: copy tile i+2 into it now
+        if (i + 2 < ntiles) {
+            const int nb = cur == 0 ? 2 : cur - 1;
+            issue_tile(tc, pc, lds0 + nb * C::BUF_BYTES);
+            next_tile(tc, pc);
+        }
+        const lds_char* kt = (const lds_char*)(smem + cur * C::BUF_BYTES);
+        const lds_char* vt = (const lds_char*)(smem + cur * C::BUF_BYTES + C::TILE_BYTES);
         const int key0 = (tq - a.tile0[pq]) * kDecTile;
         const int tile_keys = min(kDecTile, a.kv_len[pq] - key0);
         const long long kpos0 = a.kv_off[pq] + key0;
         const long long kpos_last = kpos0 + tile_keys - 1;
         const bool skip = a.causal && kpos0 > wq_last;
         if (!skip) {
-            // S^T = K Q^T: s[kb][q] = score(row, key 32kb + 16hh + q)
-            f32x16 s[2];
+            // S^T = K Q^T: s[q] = score(row, key 16hh + q)
+            f32x16 s;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int q = 0; q < 16; ++q) s[q] = 0.f;
 #pragma unroll
-                for (int q = 0; q < 16; ++q) s[kb][q] = 0.f;
-#pragma unroll
-            for (int f = 0; f < 2 * C::DSTEPS; ++f)
-                s[f % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k_frag(kt, f)),
-                                                                   as_bf16x8(qf[f / 2]), s[f % 2], 0, 0, 0);
+            for (int st = 0; st < C::DSTEPS; ++st)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k_frag(kt, st)),
+                                                            as_bf16x8(qf[st]), s, 0, 0, 0);
             if ((a.causal && kpos_last > wq_first) || tile_keys < kDecTile) {
                 const long long dq64 = qpos - kpos0;
                 const int dq = dq64 > (1 << 30) ? (1 << 30) : (dq64 < -(1 << 30) ? -(1 << 30) : (int)dq64);
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int run0 = 32 * kb + 16 * hh;
-                    int lim = tile_keys - 1 - run0;
-                    if (a.causal) lim = min(lim, dq - run0);
-                    const i32x16 ridx = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
-                    const f32x16 ninf = -INFINITY;
-                    s[kb] = ridx <= lim ? s[kb] : ninf;
-                }
+                const int run0 = 16 * hh;
+                int lim = tile_keys - 1 - run0;
+                if (a.causal) lim = min(lim, dq - run0);
+                const i32x16 ridx = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
+                const f32x16 ninf = -INFINITY;
+                s = ridx <= lim ? s : ninf;
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[kb][q]);
+            for (int q = 0; q < 16; ++q) mx = fmaxf(mx, s[q]);
             mx = half_max(mx);
             const float m_new = fmaxf(m_run, mx * a.scale_log2);
             const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -293,30 +293,29 @@ __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
                 for (int db = 0; db < C::DB; ++db) o_acc[db] *= alpha;
             }
             float rs = 0.f;
-            u32x4 pb[2][2];
+            u32x4 pb[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int j = 0; j < 2; ++j) {
+                f32x8 p;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x8 p;
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        p[u] = fast_exp2(__builtin_fmaf(s[kb][8 * j + u], a.scale_log2, -m_use));
-                        rs += p[u];
-                    }
-                    pb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
+                for (int u = 0; u < 8; ++u) {
+                    p[u] = fast_exp2(__builtin_fmaf(s[8 * j + u], a.scale_log2, -m_use));
+                    rs += p[u];
                 }
+                pb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
+            }
             l_run = l_run * alpha + rs;
             m_run = m_new;
             // O^T += V^T P^T
 #pragma unroll
-            for (int f = 0; f < 4 * C::DB; ++f) {
-                const int db = f % C::DB, j = (f / C::DB) % 2, kb = f / (2 * C::DB);
+            for (int f = 0; f < 2 * C::DB; ++f) {
+                const int db = f % C::DB, j = f / C::DB;
                 o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(v_frag(vt, f)),
-                                                                    as_bf16x8(pb[kb][j]), o_acc[db], 0, 0, 0);
+                                                                    as_bf16x8(pb[j]), o_acc[db], 0, 0, 0);
             }
         }
         next_tile(tq, pq);
+        cur = cur == 2 ? 0 : cur + 1;
     }
     wait_vmem<0>();
 
@@ -339,11 +338,19 @@ __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
         }
 }
 
-// one wave per (batch, kv head, row < R): combine the splits' states
+// one workgroup of four waves per (batch, kv head, row < R): each wave
+// combines a quarter of the splits' states against its own maximum (the
+// splits' weights computed lane-parallel into LDS first, then the o rows
+// read with several splits in flight), then the first wave combines the four
+constexpr int kMergeMaxSplits = 4096;   // weights staged in LDS per workgroup
+
 template <int D>
-__global__ void __launch_bounds__(64) decode_merge_kernel(const DecArgs a) {
+__global__ void __launch_bounds__(256) decode_merge_kernel(const DecArgs a) {
     constexpr int PER = D / 64;   // dims per lane
-    const int lane = threadIdx.x;
+    __shared__ float red_m[4], red_l[4];
+    __shared__ float red_o[4][D];
+    __shared__ float wgt[kMergeMaxSplits];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int G = a.Hq / a.Hkv, R = G * a.Tn;
     int id = blockIdx.x;
     const int r = id % R;
@@ -353,42 +360,72 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecArgs a) {
     const int RP = a.nrb * 32;
     const long long sstride = (long long)a.B * a.Hkv * RP;   // rows per split
     const long long row0 = ((long long)b * a.Hkv + g) * RP + r;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.ws_m[s * sstride + row0]);
+    const int S = a.n_splits;
+    const int s_lo = (int)((long long)S * wv / 4), s_hi = (int)((long long)S * (wv + 1) / 4);
+    float mw = -INFINITY;
+    for (int s = s_lo + lane; s < s_hi; s += 64) mw = fmaxf(mw, a.ws_m[s * sstride + row0]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
     float L = 0.f;
+    for (int s = s_lo + lane; s < s_hi; s += 64) {
+        const float ms = a.ws_m[s * sstride + row0];
+        const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - mw);
+        wgt[s] = w;
+        L += w * a.ws_l[s * sstride + row0];
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    __syncthreads();   // the weights in LDS are complete
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    if (mw != -INFINITY) {
+#pragma unroll 8
+        for (int s = s_lo; s < s_hi; ++s) {
+            const float* o = a.ws_o + (s * sstride + row0) * D + lane * PER;
+            const float w = wgt[s];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] += w * o[e];
+        }
+    }
+    if (lane == 0) {
+        red_m[wv] = mw;
+        red_l[wv] = L;
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) red_o[wv][lane * PER + e] = acc[e];
+    __syncthreads();
+    if (wv != 0) return;
+    float M = red_m[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w]);
+    float Lt = 0.f;
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < a.n_splits; ++s) {
-            const long long wr = s * sstride + row0;
-            const float ms = a.ws_m[wr];
-            const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-            L += w * a.ws_l[wr];
-            const float* o = a.ws_o + wr * D + lane * PER;
-            if constexpr (PER == 2) {
-                const f32x2 x = *reinterpret_cast<const f32x2*>(o);
-                acc[0] += w * x[0];
-                acc[1] += w * x[1];
-            } else {
-                acc[0] += w * o[0];
-            }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float sc = red_m[w] == -INFINITY ? 0.f : fast_exp2(red_m[w] - M);
+            Lt += sc * red_l[w];
+#pragma unroll
+            for (int e = 0; e < PER; ++e) o[e] += sc * red_o[w][lane * PER + e];
         }
     }
     const int qi = r / G, h = g * G + r % G;
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
     const long long oi = (((long long)b * a.Tn + qi) * a.Hq + h) * D + lane * PER;
     if (a.out_bf16) {
         __bf16* out = static_cast<__bf16*>(a.out);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) out[oi + e] = (__bf16)(acc[e] * inv);
+        for (int e = 0; e < PER; ++e) out[oi + e] = (__bf16)(o[e] * inv);
     } else {
         float* out = static_cast<float*>(a.out);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) out[oi + e] = acc[e] * inv;
+        for (int e = 0; e < PER; ++e) out[oi + e] = o[e] * inv;
     }
     if (lane == 0 && a.lse)
-        a.lse[((long long)b * a.Hq + h) * a.Tn + qi] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+        a.lse[((long long)b * a.Hq + h) * a.Tn + qi] = Lt > 0.f ? (M + __log2f(Lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -409,10 +446,10 @@ int launch_decode_split(const DecArgs& a, int D, void* stream) {
 int launch_decode_merge(const DecArgs& a, int D, void* stream) {
     const int grid = a.B * a.Hkv * (a.Hq / a.Hkv) * a.Tn;
     if (D == 128)
-        hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64), 0,
+        hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(256), 0,
                            static_cast<hipStream_t>(stream), a);
     else if (D == 64)
-        hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(grid), dim3(64), 0,
+        hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(grid), dim3(256), 0,
                            static_cast<hipStream_t>(stream), a);
     else
         return (int)hipErrorInvalidValue;

@@ -203,9 +203,9 @@ def test_decode_errors_and_workspace_size():
     offs = (I64 * 3)(0, 1000, 1000)
     ptrs = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
     nb = I64(0)
-    # workspace size: 17 tiles; (B=1, Hkv=2, one 32-row block) -> splits of one tile
+    # workspace size: 34 tiles of 32 keys; (B=1, Hkv=2, one 32-row block) -> splits of one tile
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, lens, 3, ctypes.byref(nb)) == 0
-    assert nb.value == 17 * 1 * 2 * 1 * 32 * (128 + 2) * 4
+    assert nb.value == 34 * 1 * 2 * 1 * 32 * (128 + 2) * 4
     assert L.cakv_decode_workspace_size(0, 8, 2, 4, 128, lens, 3, ctypes.byref(nb)) == 0
     assert nb.value == 0
     assert L.cakv_decode_workspace_size(1, 8, 3, 4, 128, lens, 3, ctypes.byref(nb)) == 2
@@ -214,7 +214,7 @@ def test_decode_errors_and_workspace_size():
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, None, 3, ctypes.byref(nb)) == 1
     bad = (I64 * 1)(-1)
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, bad, 1, ctypes.byref(nb)) == 2
-    need = 17 * 2 * 32 * 130 * 4
+    need = 34 * 2 * 32 * 130 * 4
 
     def dec(q=FAKE, k=ptrs, v=ptrs, n=3, dtype=1, B=1, D=128, out=FAKE, odt=0, ws=FAKE,
             wsb=need):
