@@ -42,6 +42,8 @@ CEILING_ITERS = 200000   # ~0.35-0.5 s per cakv_diag_mfma_burn launch
 METRIC = "local-shard attention TFLOP/s (useful causal FLOPs), % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "fwd_bf16.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "decode_bf16.hip")
 
 
 def log(msg):
@@ -62,8 +64,8 @@ def useful_flops(w, ranks) -> int:
     return sum(4 * w.D * allowed_pairs(w, r) * w.B * w.Hq for r in ranks)
 
 
-def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_hash(path: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
 def traffic_for(workload_name: str):
@@ -76,6 +78,18 @@ def traffic_for(workload_name: str):
     if rec.get("kernel_sha") != kernel_hash() or rec.get("workload") != workload_name:
         return None
     return rec.get("bytes_per_launch")
+
+
+def decode_traffic(workload_name: str):
+    """HBM bytes per decode call (split + merge kernels) from the committed
+    counter profile, if taken on this workload and the current kernel source."""
+    try:
+        rec = json.load(open(DECODE_TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash(DECODE_SRC) or rec.get("workload") != workload_name:
+        return None
+    return rec.get("bytes_per_call")
 
 
 def calibrate_copy(nbytes: int):
@@ -161,7 +175,7 @@ def bench_decode(args):
         "new_tokens_per_s": round(w.B * w.Tn / (ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic(w.name),
                      "bytes_per_call": alg, "avg_call_ms": round(ms, 4),
                      "workspace_bytes": nbytes},
     }
