@@ -30,7 +30,7 @@ EXPORTED = (
     "cakv_abi_version", "cakv_status_str", "cakv_last_error", "cakv_classify_block",
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
     "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
-    "cakv_decode_workspace_size",
+    "cakv_decode_workspace_size", "cakv_forward_blocks",
 )
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
 
@@ -68,6 +68,7 @@ def _load_lib():
         "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, P], I),
         "cakv_diag_mfma_burn": ([I, I64, P, P], I),
         "cakv_decode": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P], I),
+        "cakv_forward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, P], I),
         "cakv_decode_workspace_size": ([I, I, I, I, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -260,3 +261,31 @@ def cakv_decode(q, k_portions: Sequence, v_portions: Sequence, kv_offsets: Seque
                             D, int(q_offset), int(causal), float(scale), _ptr(out),
                             _dtype_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                             _stream(stream)), "cakv_decode")
+
+
+def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: Sequence[int],
+                        q_offset: int, causal: bool, out, lse=None, scale: float = 0.0,
+                        tile_counters=None, stream=None):
+    """Queries q [B, Tq, Hq, D] at positions q_offset ... against blocks
+    [B, L_t, Hkv, D] of any lengths at global offsets kv_offsets[t], in the
+    order given; writes out [B, Tq, Hq, D] and lse [B, Hq, Tq]."""
+    _contig(q, out, lse, *k_blocks, *v_blocks)
+    B, Tq, Hq, D = q.shape
+    n = len(k_blocks)
+    if len(v_blocks) != n or len(kv_offsets) != n or n == 0:
+        raise ValueError("need the same positive number of K blocks, V blocks and offsets")
+    Hkv = k_blocks[0].shape[2]
+    lens = []
+    for kb, vb in zip(k_blocks, v_blocks):
+        if kb.shape != vb.shape or kb.shape[0] != B or kb.shape[2] != Hkv or kb.shape[3] != D \
+                or kb.dtype != q.dtype or vb.dtype != q.dtype:
+            raise ValueError("every block must be [B, L_t, Hkv, D] with the query dtype")
+        lens.append(int(kb.shape[1]))
+    karr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in k_blocks])
+    varr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in v_blocks])
+    larr = (ctypes.c_int64 * n)(*lens)
+    oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
+    _check(_lib.cakv_forward_blocks(_ptr(q), karr, varr, larr, oarr, n, _dtype_code(q), B, Hq,
+                                    Hkv, Tq, D, int(q_offset), int(causal), float(scale),
+                                    _ptr(out), _dtype_code(out), _ptr(lse), _ptr(tile_counters),
+                                    _stream(stream)), "cakv_forward_blocks")

@@ -316,6 +316,60 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
 }
 
+cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
+                                const void* const* v_blocks_host, const int64_t* kv_len_host,
+                                const int64_t* kv_off_host, int n_blocks, int dtype, int B,
+                                int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
+                                float scale, void* out, int out_dtype, float* lse,
+                                int64_t* tile_counters, void* stream) {
+    cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
+    if (s != CAKV_OK) return s;
+    if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
+        return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
+    if (n_blocks < 1 || n_blocks > CAKV_MAX_CHUNKS)
+        return fail(CAKV_ERR_RANGE, "n_blocks=%d outside [1, %d]", n_blocks, CAKV_MAX_CHUNKS);
+    if (!kv_len_host || !kv_off_host) return fail(CAKV_ERR_NULL, "block length / offset array is NULL");
+    for (int t = 0; t < n_blocks; ++t)
+        if (kv_len_host[t] < 0 || kv_len_host[t] > 2147483647LL)
+            return fail(CAKV_ERR_SHAPE, "block %d length %lld out of range", t,
+                        (long long)kv_len_host[t]);
+    if (B == 0 || Tq == 0) return ok();
+    if (!q || !out) return fail(CAKV_ERR_NULL, "q or out is NULL");
+    if (!k_blocks_host || !v_blocks_host) return fail(CAKV_ERR_NULL, "block pointer array is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(CAKV_ERR_ALIGN, "q/out not 16-byte aligned");
+    if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
+        return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
+
+    cakv::FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    int n = 0;
+    for (int t = 0; t < n_blocks; ++t) {
+        if (classify(q_offset, Tq, kv_off_host[t], kv_len_host[t], causal) == CAKV_SKIP) continue;
+        const void* kp = k_blocks_host[t];
+        const void* vp = v_blocks_host[t];
+        if (!kp || !vp) return fail(CAKV_ERR_NULL, "block %d pointer is NULL", t);
+        if (!aligned16(kp) || !aligned16(vp))
+            return fail(CAKV_ERR_ALIGN, "block %d not 16-byte aligned", t);
+        a.k[n] = kp;
+        a.v[n] = vp;
+        a.kv_off[n] = kv_off_host[t];
+        a.kv_len[n] = (int)kv_len_host[t];
+        ++n;
+    }
+    a.q = q;
+    a.n_blocks = n;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq;
+    a.q_off = q_offset;
+    a.scale_log2 = resolve_scale(scale, D) * 1.4426950408889634f;
+    a.causal = causal ? 1 : 0;
+    a.out = out;
+    a.out_bf16 = out_dtype == CAKV_BF16;
+    a.lse = lse;
+    a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
+    set_grid(a, dtype, D);
+    return hip_status(launch_fwd(a, dtype, D, stream), "forward_blocks launch");
+}
+
 cakv_status cakv_decode_workspace_size(int B, int Hq, int Hkv, int Tn, int D,
                                        const int64_t* kv_len_host, int n_portions,
                                        int64_t* bytes_host) {

@@ -195,6 +195,33 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
                                      void* stream);
 
 /*
+ * The general form of cakv_local_shard_forward: Tq queries at global
+ * positions q_offset + row against n_blocks key/value blocks of any lengths
+ * at any global offsets, folded in the order given with the running state
+ * on chip, then finalised. It covers the cases the ring of equal chunks does
+ * not: unequal chunks, keys and values appended across turns, blocks that
+ * straddle the query range (page sections "Causal attention gives us
+ * another optimization" for the per-position rule and "Training and
+ * inference stress this dimension differently" for a KV history that grows).
+ * Blocks whose keys all lie after every query (causal) are never read; a
+ * block straddling a query's position is masked per tile.
+ * q: [B, Tq, Hq, D]; k_blocks_host, v_blocks_host: HOST arrays of n_blocks
+ *   device pointers, block t = [B, kv_len_host[t], Hkv, D] with key 0 at
+ *   global position kv_off_host[t] (HOST int64 arrays; an empty block's
+ *   pointers may be NULL);
+ * out, lse, tile_counters, dtype, scale: as for cakv_local_shard_forward.
+ * Errors: as for cakv_block_update, plus n_blocks outside
+ * [1, CAKV_MAX_CHUNKS], a block length outside [0, 2^31 - 1], a NULL block
+ * pointer that would be read.
+ */
+cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
+                                const void* const* v_blocks_host, const int64_t* kv_len_host,
+                                const int64_t* kv_off_host, int n_blocks, int dtype, int B,
+                                int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
+                                float scale, void* out, int out_dtype, float* lse,
+                                int64_t* tile_counters, void* stream);
+
+/*
  * Decode over a KV history held in portions (page section "Training and
  * inference stress this dimension differently": during inference each device
  * holds one portion of a long conversation's keys and values, the new query

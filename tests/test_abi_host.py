@@ -231,3 +231,25 @@ def test_decode_errors_and_workspace_size():
     assert dec(q=MIS) == 4
     assert dec(k=None) == 1
     assert dec(B=0, q=None, out=None, ws=None) == 0   # nothing to do
+
+
+def test_forward_blocks_errors():
+    I64 = ctypes.c_int64
+    lens = (I64 * 2)(100, 0)
+    offs = (I64 * 2)(0, 100)
+    ptrs = (ctypes.c_void_p * 2)(FAKE, None)
+
+    def fb(q=FAKE, n=2, dtype=1, B=1, D=128, Hkv=2, out=FAKE, odt=0, ln=lens, k=ptrs):
+        return L.cakv_forward_blocks(q, k, ptrs, ln, offs, n, dtype, B, 8, Hkv, 50, D, 100, 1, 0.0,
+                                     out, odt, None, None, None)
+    assert fb(dtype=5) == 3
+    assert fb(odt=5) == 3
+    assert fb(n=0) == 5
+    assert fb(n=65) == 5
+    assert fb(D=96) == 2
+    assert fb(Hkv=3) == 2
+    assert fb(ln=(I64 * 2)(-1, 0)) == 2
+    assert fb(q=None) == 1
+    assert fb(k=None) == 1
+    assert fb(q=MIS) == 4
+    assert fb(B=0, q=None, out=None) == 0
