@@ -74,6 +74,10 @@ def _load():
         lib.oracle_classify.restype = I
         lib.oracle_lse_merge.argtypes = [P, P, P, P, I64, I64, P, P]
         lib.oracle_lse_merge.restype = None
+        lib.oracle_attention_backward.argtypes = [
+            P, I, P, P, I, P, I, I64, I64, I64, I64, I64, I64, I64, I64, I,
+            ctypes.c_double, P, P, P]
+        lib.oracle_attention_backward.restype = I
         _lib = lib
     return _lib
 
@@ -188,6 +192,33 @@ def classify(Tq, q_off, starts, lens, *, k_off=0, causal=True, B=1, Hq=1,
     if rc != 0:
         raise ValueError("oracle_classify: bad arguments")
     return cls, pairs, tiles
+
+
+def attention_backward(q, k, v, dout, *, q_off=0, k_off=0, causal=True, scale=None,
+                       threads=None):
+    """O4: fp64 gradients (dq [B,Tq,Hq,D], dk, dv [B,Tk,Hkv,D]) of
+    sum(out * dout) for out = attention(q, k, v) as in O1."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dout = np.ascontiguousarray(dout)
+    B, Tq, Hq, D = q.shape
+    Bk, Tk, Hkv, Dk = k.shape
+    assert Bk == B and Dk == D and v.shape == k.shape and dout.shape == q.shape
+    fq, fk, fd = _dtype_flag(q), _dtype_flag(k), _dtype_flag(dout)
+    assert _dtype_flag(v) == fk
+    if scale is None:
+        scale = default_scale(D)
+    dq = np.zeros((B, Tq, Hq, D), np.float64)
+    dk = np.zeros((B, Tk, Hkv, D), np.float64)
+    dv = np.zeros((B, Tk, Hkv, D), np.float64)
+    _set_threads(threads)
+    rc = _load().oracle_attention_backward(
+        _ptr(q), fq, _ptr(k), _ptr(v), fk, _ptr(dout), fd, B, Hq, Hkv, Tq, Tk, D,
+        q_off, k_off, int(bool(causal)), float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle_attention_backward: bad arguments")
+    return dq, dk, dv
 
 
 def lse_merge(o_a, lse_a, o_b, lse_b):

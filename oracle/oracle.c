@@ -301,3 +301,85 @@ void oracle_lse_merge(const double* o_a, const double* lse_a,
         lse_out[r] = lse;
     }
 }
+
+/*
+ * O4: gradients of the definition O1 (the pages give no backward formulas;
+ * these are the chain rule applied to out_i = sum_j p_ij v_j with
+ * p_ij = e^{s_ij} / sum_j' e^{s_ij'} over the allowed keys and
+ * s_ij = scale q_i . k_j). With dout the gradient of a loss with respect to
+ * out, for each query row i:
+ *   dv_j  += p_ij dout_i                      (every allowed key j)
+ *   dp_ij  = dout_i . v_j
+ *   ds_ij  = p_ij (dp_ij - sum_j' p_ij' dp_ij')
+ *   dq_i   = scale sum_j ds_ij k_j
+ *   dk_j  += scale ds_ij q_i
+ * Rows of the query heads that share a key/value head all add into that
+ * head's dk, dv. dq: [B, Tq, Hq, D]; dk, dv: [B, Tk, Hkv, D]; all fp64,
+ * overwritten. Parallel over (batch, key/value head) so that no two threads
+ * add into the same dk, dv rows. Returns 0, or -1 on a bad argument.
+ */
+int oracle_attention_backward(const void* q, int q_bf16, const void* k,
+                              const void* v, int kv_bf16, const void* dout,
+                              int dout_bf16, int64_t B, int64_t Hq, int64_t Hkv,
+                              int64_t Tq, int64_t Tk, int64_t D, int64_t q_off,
+                              int64_t k_off, int causal, double scale,
+                              double* dq, double* dk, double* dv) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Tq < 0 || Tk < 0 || D <= 0)
+        return -1;
+    const int64_t group = Hq / Hkv;
+    memset(dq, 0, sizeof(double) * (size_t)(B * Tq * Hq * D));
+    memset(dk, 0, sizeof(double) * (size_t)(B * Tk * Hkv * D));
+    memset(dv, 0, sizeof(double) * (size_t)(B * Tk * Hkv * D));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+        const int64_t b = bg / Hkv, g = bg % Hkv;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Tk > 0 ? Tk : 1));
+        double* p = (double*)malloc(sizeof(double) * (size_t)(Tk > 0 ? Tk : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(Tk > 0 ? Tk : 1));
+        for (int64_t h = g * group; h < (g + 1) * group; ++h) {
+            for (int64_t i = 0; i < Tq; ++i) {
+                const int64_t qpos = q_off + i;
+                double M = -INFINITY;
+                for (int64_t j = 0; j < Tk; ++j) {
+                    if (allowed(causal, k_off + j, qpos)) {
+                        s[j] = score(q, q_bf16, k, kv_bf16, b, i, h, j, g, Tq, Hq,
+                                     Tk, Hkv, D, scale);
+                        if (s[j] > M) M = s[j];
+                    }
+                }
+                if (M == -INFINITY) continue;   /* no allowed key: no gradient */
+                double Z = 0.0;
+                for (int64_t j = 0; j < Tk; ++j) {
+                    p[j] = allowed(causal, k_off + j, qpos) ? exp(s[j] - M) : 0.0;
+                    Z += p[j];
+                }
+                double pdp = 0.0;
+                for (int64_t j = 0; j < Tk; ++j) {
+                    p[j] /= Z;
+                    dp[j] = 0.0;
+                    if (!allowed(causal, k_off + j, qpos)) continue;
+                    for (int64_t c = 0; c < D; ++c)
+                        dp[j] += load_elem(dout, dout_bf16, qk_index(b, i, h, c, Tq, Hq, D)) *
+                                 load_elem(v, kv_bf16, qk_index(b, j, g, c, Tk, Hkv, D));
+                    pdp += p[j] * dp[j];
+                }
+                double* dqi = dq + qk_index(b, i, h, 0, Tq, Hq, D);
+                for (int64_t j = 0; j < Tk; ++j) {
+                    if (!allowed(causal, k_off + j, qpos)) continue;
+                    const double ds = p[j] * (dp[j] - pdp);
+                    double* dkj = dk + qk_index(b, j, g, 0, Tk, Hkv, D);
+                    double* dvj = dv + qk_index(b, j, g, 0, Tk, Hkv, D);
+                    for (int64_t c = 0; c < D; ++c) {
+                        dqi[c] += scale * ds * load_elem(k, kv_bf16, qk_index(b, j, g, c, Tk, Hkv, D));
+                        dkj[c] += scale * ds * load_elem(q, q_bf16, qk_index(b, i, h, c, Tq, Hq, D));
+                        dvj[c] += p[j] * load_elem(dout, dout_bf16, qk_index(b, i, h, c, Tq, Hq, D));
+                    }
+                }
+            }
+        }
+        free(s);
+        free(p);
+        free(dp);
+    }
+    return 0;
+}

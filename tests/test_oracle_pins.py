@@ -365,3 +365,90 @@ def test_classify_respects_key_offset():
         b = oracle.classify(C, (r - 1) * C, starts, lens, k_off=0, causal=True)
         for x, y in zip(a, b):
             np.testing.assert_array_equal(x, y)
+
+
+# ---- O4: gradients of the definition --------------------------------------
+
+def _loss(q, k, v, dout, q_off, causal):
+    """sum(out * dout) with out from O1 (fp64 on the stored inputs)."""
+    B, Tq, Hq, D = q.shape
+    o, _ = oracle.attention(q, k, v, q_off=q_off, causal=causal)
+    # O1 rows come b-major, then head, then position
+    o = o.reshape(B, Hq, Tq, D).transpose(0, 2, 1, 3)
+    return float((o * dout.astype(np.float64)).sum())
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_o4_matches_finite_differences(causal):
+    """Central differences of sum(out * dout) through O1, element by element
+    on a sample of q, k and v entries (perturbations taken exactly as the
+    difference of the two stored fp32 values)."""
+    rng = np.random.default_rng(41 + causal)
+    B, Tq, Tk, Hq, Hkv, D = 1, 5, 7, 4, 2, 8
+    q = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
+    dout = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
+    q_off = 3   # queries at 3..7 see keys 0..min(i, 6) when causal
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, q_off=q_off, causal=causal)
+    eps = 1.0 / 512
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        idx = list(np.ndindex(x.shape))
+        pick = [idx[i] for i in rng.choice(len(idx), 24, replace=False)]
+        for e in pick:
+            xp, xm = x.copy(), x.copy()
+            xp[e] = np.float32(x[e] + eps)
+            xm[e] = np.float32(x[e] - eps)
+            h = float(xp[e]) - float(xm[e])
+            args = {"q": q, "k": k, "v": v}
+            lp = _loss(*[xp if n == name else args[n] for n in ("q", "k", "v")], dout, q_off, causal)
+            lm = _loss(*[xm if n == name else args[n] for n in ("q", "k", "v")], dout, q_off, causal)
+            fd = (lp - lm) / h
+            assert abs(fd - g[e]) <= 2e-5 * max(1.0, abs(fd)), (name, e, fd, g[e])
+
+
+def test_o4_single_key_closed_form():
+    """One key: p = 1, so dv = the sum of dout over the query heads that read
+    it, and dq = dk = 0."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 1, 2, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 1, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 1, 8)).astype(np.float32)
+    dout = rng.standard_normal((1, 1, 2, 8)).astype(np.float32)
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, causal=False)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    np.testing.assert_allclose(dv[0, 0, 0], dout[0, 0].astype(np.float64).sum(axis=0), rtol=0,
+                               atol=1e-12)
+
+
+def test_o4_invariants_bidirectional():
+    """Every row sees every key: shifting all keys by one vector leaves the
+    output unchanged, so the key gradients of each head sum to zero; the
+    weights of a row sum to 1, so the value gradients sum to the rows' dout."""
+    rng = np.random.default_rng(44)
+    B, Tq, Tk, Hq, Hkv, D = 2, 6, 9, 4, 2, 16
+    q = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
+    dout = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, causal=False)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-12
+    G = Hq // Hkv
+    want = dout.astype(np.float64).reshape(B, Tq, Hkv, G, D).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), want, rtol=0, atol=1e-11)
+
+
+def test_o4_causal_future_keys_get_nothing():
+    """Causal: keys after every query get zero gradients, and a query's
+    gradient does not move when a later key changes."""
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((1, 4, 2, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 10, 2, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 10, 2, 8)).astype(np.float32)
+    dout = rng.standard_normal((1, 4, 2, 8)).astype(np.float32)
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, q_off=2, causal=True)
+    assert not dk[0, 6:].any() and not dv[0, 6:].any()      # keys 6..9 follow queries 2..5
+    k2 = k.copy()
+    k2[0, 5] += 1.0                                           # key 5: seen by query 5 only
+    dq2, _, _ = oracle.attention_backward(q, k2, v, dout, q_off=2, causal=True)
+    assert np.array_equal(dq[0, :3], dq2[0, :3]) and not np.array_equal(dq[0, 3], dq2[0, 3])
