@@ -106,6 +106,90 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
 
 
+def bench_backward(args):
+    """Gradients of one rank's share (dq, dk, dv from out, lse and a seeded
+    upstream gradient): useful FLOPs = 2.5 x the forward's (five products of
+    2 d_k FLOPs per allowed pair: the score recomputation, dP, dV, dQ, dK)."""
+    import numpy as np
+    import torch
+
+    import cakv_synth as syn
+    import context_attention_kv_amd as cakv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = syn.scaled(syn.WORKLOADS[5], name="backward-T131072-N8-Hq32-Hkv8-d128-bf16-causal",
+                   T=131072)
+    r = w.ranks[-1]
+    C = w.C
+    log(f"generating {w.name}")
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+    kd, vd = dev(syn.make_kv_full(w, "k")), dev(syn.make_kv_full(w, "v"))
+    qd = dev(syn.make_q_local(w, r))
+    dout = np.empty((w.B, C, w.Hq, w.D), np.uint16)
+    syn.fill(dout, seed=w.seed, tensor=7)
+    dod = dev(dout)
+    order = [(r - k) % w.N for k in range(w.N)]
+    kb = [kd[:, j * C:(j + 1) * C] for j in order]
+    vb = [vd[:, j * C:(j + 1) * C] for j in order]
+    offs = [j * C for j in order]
+    out = torch.empty((w.B, C, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
+    cakv.cakv_forward_blocks(qd, kb, vb, offs, r * C, w.causal, out, lse)
+    dq = torch.empty_like(out)
+    dk = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in kb]
+    dv = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in kb]
+    ws = torch.empty(w.B * w.Hq * C, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        cakv.cakv_backward_blocks(qd, kb, vb, offs, r * C, w.causal, out, lse, dod, dq, dk, dv,
+                                  workspace=ws)
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = 2.5 * useful_flops(w, [r])
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "backward of one rank's share: useful TFLOP/s (2.5x the forward's FLOPs)",
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "N": w.N,
+                   "chunk": C, "d_k": w.D, "causal": w.causal, "ranks": [r]},
+        "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel + bwd_dkdv_kernel (+ bwd_delta)",
+                     "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_call_ms": round(ms, 4), "flops_per_call": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_decode(args):
     """Decode over a KV history in portions (HBM-bound): new tokens per second
     and algorithmic HBM bytes (the whole history's K and V, the new queries,
@@ -194,6 +278,9 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained matrix-core rate measurement")
+    ap.add_argument("--backward", action="store_true",
+                    help="time cakv_backward_blocks on the 131,072-token causal context "
+                         "(the million-token workload's shape at 1/8 length) instead")
     ap.add_argument("--decode", type=int, default=0, choices=[0, 1, 2], metavar="CFG",
                     help="time cakv_decode on decode workload CFG (2 = million-token "
                          "history) instead of the forward path")
@@ -206,6 +293,9 @@ def main():
         return
     if args.decode:
         bench_decode(args)
+        return
+    if args.backward:
+        bench_backward(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -30,7 +30,8 @@ EXPORTED = (
     "cakv_abi_version", "cakv_status_str", "cakv_last_error", "cakv_classify_block",
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
     "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
-    "cakv_decode_workspace_size", "cakv_forward_blocks",
+    "cakv_decode_workspace_size", "cakv_forward_blocks", "cakv_backward_blocks",
+    "cakv_backward_workspace_size",
 )
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
 
@@ -69,6 +70,9 @@ def _load_lib():
         "cakv_diag_mfma_burn": ([I, I64, P, P], I),
         "cakv_decode": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P], I),
         "cakv_forward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, P], I),
+        "cakv_backward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, P, P, P, P, P,
+                                  P, I64, P], I),
+        "cakv_backward_workspace_size": ([I, I, I, P], I),
         "cakv_decode_workspace_size": ([I, I, I, I, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -289,3 +293,36 @@ def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: S
                                     Hkv, Tq, D, int(q_offset), int(causal), float(scale),
                                     _ptr(out), _dtype_code(out), _ptr(lse), _ptr(tile_counters),
                                     _stream(stream)), "cakv_forward_blocks")
+
+
+def cakv_backward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: Sequence[int],
+                         q_offset: int, causal: bool, out, lse, dout, dq, dk_blocks: Sequence,
+                         dv_blocks: Sequence, workspace=None, scale: float = 0.0, stream=None):
+    """Gradients of cakv_forward_blocks: dq [B, Tq, Hq, D], dk/dv blocks
+    [B, L_t, Hkv, D] (fp32, overwritten) from out/lse of the forward and the
+    bf16 upstream gradient dout."""
+    _contig(q, out, lse, dout, dq, *k_blocks, *v_blocks, *dk_blocks, *dv_blocks)
+    B, Tq, Hq, D = q.shape
+    n = len(k_blocks)
+    if not (len(v_blocks) == len(kv_offsets) == len(dk_blocks) == len(dv_blocks) == n) or n == 0:
+        raise ValueError("need the same positive number of blocks, offsets and gradient blocks")
+    Hkv = k_blocks[0].shape[2]
+    lens = [int(t.shape[1]) for t in k_blocks]
+    for kb, vb, gk, gv in zip(k_blocks, v_blocks, dk_blocks, dv_blocks):
+        if not (kb.shape == vb.shape == gk.shape == gv.shape) or kb.shape[0] != B \
+                or kb.shape[2] != Hkv or kb.shape[3] != D:
+            raise ValueError("blocks and their gradients must all be [B, L_t, Hkv, D]")
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(B * Hq * Tq, 4), dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    def arr(ts):
+        return (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in ts])
+    larr = (ctypes.c_int64 * n)(*lens)
+    oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
+    _check(_lib.cakv_backward_blocks(_ptr(q), arr(k_blocks), arr(v_blocks), larr, oarr, n,
+                                     _dtype_code(q), B, Hq, Hkv, Tq, D, int(q_offset),
+                                     int(causal), float(scale), _ptr(out), _ptr(lse), _ptr(dout),
+                                     _ptr(dq), arr(dk_blocks), arr(dv_blocks), _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "cakv_backward_blocks")

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcakv.so")
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "state_ops.hip", "diag_mfma.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "state_ops.hip", "diag_mfma.hip", "decode_bf16.hip", "bwd_bf16.hip"]
 ARCH = "gfx950"
 
 

@@ -12,6 +12,7 @@
 
 #include "cakv.h"
 #include "cakv_diag.h"
+#include "bwd_args.h"
 #include "decode_args.h"
 #include "fwd_args.h"
 
@@ -368,6 +369,93 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     set_grid(a, dtype, D);
     return hip_status(launch_fwd(a, dtype, D, stream), "forward_blocks launch");
+}
+
+cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host) {
+    if (!bytes_host) return fail(CAKV_ERR_NULL, "bytes_host is NULL");
+    if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
+    *bytes_host = (int64_t)B * Hq * Tq * 4;
+    return ok();
+}
+
+cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host,
+                                 const void* const* v_blocks_host, const int64_t* kv_len_host,
+                                 const int64_t* kv_off_host, int n_blocks, int dtype, int B,
+                                 int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
+                                 float scale, const float* out, const float* lse,
+                                 const void* dout, float* dq, float* const* dk_blocks_host,
+                                 float* const* dv_blocks_host, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+    cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
+    if (s != CAKV_OK) return s;
+    if (dtype != CAKV_BF16) return fail(CAKV_ERR_DTYPE, "cakv_backward_blocks takes bf16 inputs only");
+    if (n_blocks < 1 || n_blocks > CAKV_MAX_CHUNKS)
+        return fail(CAKV_ERR_RANGE, "n_blocks=%d outside [1, %d]", n_blocks, CAKV_MAX_CHUNKS);
+    if (!kv_len_host || !kv_off_host) return fail(CAKV_ERR_NULL, "block length / offset array is NULL");
+    long long key_tiles = 0;
+    for (int t = 0; t < n_blocks; ++t) {
+        if (kv_len_host[t] < 0 || kv_len_host[t] > 2147483647LL - cakv::kBwdKeyTile)
+            return fail(CAKV_ERR_SHAPE, "block %d length %lld out of range", t,
+                        (long long)kv_len_host[t]);
+        key_tiles += (kv_len_host[t] + cakv::kBwdKeyTile - 1) / cakv::kBwdKeyTile;
+    }
+    if (B == 0) return ok();
+    if (!k_blocks_host || !v_blocks_host || !dk_blocks_host || !dv_blocks_host)
+        return fail(CAKV_ERR_NULL, "block pointer array is NULL");
+    if (Tq > 0 && (!q || !out || !lse || !dout || !dq))
+        return fail(CAKV_ERR_NULL, "q, out, lse, dout or dq is NULL");
+    if (Tq > 0 && !workspace) return fail(CAKV_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < (int64_t)B * Hq * Tq * 4)
+        return fail(CAKV_ERR_SHAPE, "workspace of %lld bytes, %lld needed",
+                    (long long)workspace_bytes, (long long)B * Hq * Tq * 4);
+    if ((Tq > 0 && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq))) ||
+        !aligned16(workspace))
+        return fail(CAKV_ERR_ALIGN, "q/out/dout/dq/workspace not 16-byte aligned");
+    if (key_tiles > 2147483647LL / ((long long)B * Hkv))
+        return fail(CAKV_ERR_SHAPE, "too many key tiles");
+
+    cakv::BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    int kt = 0;
+    for (int t = 0; t < n_blocks; ++t) {
+        a.kt0[t] = kt;
+        a.kv_len[t] = (int)kv_len_host[t];
+        a.kv_off[t] = kv_off_host[t];
+        if (kv_len_host[t] > 0) {
+            if (!k_blocks_host[t] || !v_blocks_host[t] || !dk_blocks_host[t] || !dv_blocks_host[t])
+                return fail(CAKV_ERR_NULL, "block %d pointer is NULL", t);
+            if (!aligned16(k_blocks_host[t]) || !aligned16(v_blocks_host[t]) ||
+                !aligned16(dk_blocks_host[t]) || !aligned16(dv_blocks_host[t]))
+                return fail(CAKV_ERR_ALIGN, "block %d not 16-byte aligned", t);
+            a.k[t] = k_blocks_host[t];
+            a.v[t] = v_blocks_host[t];
+            a.dk[t] = dk_blocks_host[t];
+            a.dv[t] = dv_blocks_host[t];
+        }
+        kt += (int)((kv_len_host[t] + cakv::kBwdKeyTile - 1) / cakv::kBwdKeyTile);
+    }
+    a.kt0[n_blocks] = kt;
+    a.n_blocks = n_blocks;
+    a.q = q;
+    a.dout = dout;
+    a.out = out;
+    a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq;
+    a.q_off = q_offset;
+    a.scale = resolve_scale(scale, D);
+    a.scale_log2 = a.scale * 1.4426950408889634f;
+    a.causal = causal ? 1 : 0;
+    a.delta = static_cast<float*>(workspace);
+    a.dq = dq;
+    const int G = Hq / Hkv;
+    const long long npblk = (Tq + 31) / 32;
+    a.wg_per_bg = (int)((G * npblk + 3) / 4);
+    if (Tq == 0) {
+        // no queries: every key gradient is zero (the dK/dV kernel visits no query tile)
+        a.wg_per_bg = 0;
+    }
+    if (kt == 0 && Tq == 0) return ok();
+    return hip_status(cakv::launch_bwd(a, D, stream), "backward launch");
 }
 
 cakv_status cakv_decode_workspace_size(int B, int Hq, int Hkv, int Tn, int D,

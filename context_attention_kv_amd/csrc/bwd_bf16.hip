@@ -1,0 +1,517 @@
+// bwd_bf16.hip -- gradients of one rank's attention against key/value blocks.
+//
+// The pages use sequence parallelism for training as well as inference (web
+// page "Sequence parallelism -- splitting the token dimension across GPUs",
+// section "Training and inference stress this dimension differently") but
+// give no backward formulas; these kernels apply the chain rule to the
+// definition softmax(Q K^T / sqrt(d_k)) V (section "Attention wants keys and
+// values from other tokens"), with the probabilities recomputed from the
+// forward's log-sum-exp instead of stored:
+//   p_ij = e^{s_ij - lse_i},  delta_i = dout_i . out_i,
+//   ds_ij = p_ij (dout_i . v_j - delta_i),
+//   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,  dv_j = sum_i p_ij dout_i,
+// the causal rule by global position as in the forward.
+//
+// bwd_delta_kernel: delta per query row (one wave per row).
+// bwd_dq_kernel: query-stationary, 4 waves per workgroup, each wave 32 rows of
+//   one query head (grouped heads share the workgroup's K/V tiles). Per
+//   64-key tile, staged in LDS through registers (double buffer):
+//   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 (K, V as A
+//   operands, Q^T and dO^T in registers as B), dS = P (dP - delta), then
+//   dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16.
+// bwd_dkdv_kernel: key-stationary, 4 waves of 32 keys (K^T and V^T in
+//   registers as B operands) over every 32-row query tile of the kv head's
+//   query heads, staged in LDS: S = Q K^T and dP = dO V^T (query rows in
+//   output registers), dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
+//   read through ds_read_b64_tr_b16.
+#include <hip/hip_runtime.h>
+
+#include "bwd_args.h"
+
+namespace cakv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
+constexpr float kLog2e = 1.44269504088896341f;
+
+// Row i of a 32-row A operand lands in output row i, which the 32x32 layout
+// gives to half-wave (i/4)%2 at register 4*(i/8) + i%4; reading row
+// 16*((i/4)%2) + 4*(i/8) + i%4 of a tile into operand row i leaves rows
+// 16h..16h+15 in registers 0..15 of half-wave h, in order.
+__device__ __forceinline__ int perm_row(int i) {
+    return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+// XOR swizzle of the 16-byte units of a tile row (the forward kernel's
+// K-tile layout: conflict-free 16-byte operand reads)
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128)
+        return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
+    else
+        return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D>
+struct BCfg {
+    static constexpr int DSTEPS = D / 16;
+    static constexpr int DB = D / 32;
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int UNITS = D / 8;   // 16-byte units per row
+};
+
+// 16-byte operand unit `unit` of tile row `row` (swizzled layout)
+template <int D>
+__device__ __forceinline__ u32x4 tile_unit(const lds_char* t, int row, int unit) {
+    return *(const lds_u32x4*)(t + row * BCfg<D>::ROW_BYTES + 16 * (unit ^ swz<D>(row)));
+}
+// Transposed operand (rows as the contraction index): fragment f = (j, db)
+// of a 32-row block, through ds_read_b64_tr_b16. In each 16-lane group g16,
+// source lane 4k + q points at row base + k and dims 16 (g16 % 2) + 4q .. +3
+// of the 32-dim block; the group receives 4 consecutive rows of one dim per
+// lane. Rows of step j: 8j + 16 (g16 / 2) + k, and 4 more for the high half.
+template <int D>
+__device__ __forceinline__ u32x4 tile_tr(const lds_char* t, int lane, int j, int db) {
+    constexpr int RB = BCfg<D>::ROW_BYTES;
+    const int g16 = lane >> 4, src = lane & 15;
+    const int row = 8 * j + 16 * (g16 >> 1) + (src >> 2);
+    const int d = 32 * db + 16 * (g16 & 1) + 4 * (src & 3);
+    const int lo = row * RB + 16 * ((d >> 3) ^ swz<D>(row)) + 2 * (d & 7);
+    const int hi = (row + 4) * RB + 16 * ((d >> 3) ^ swz<D>(row + 4)) + 2 * (d & 7);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + lo));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + hi));
+    const u32x2 a2 = __builtin_bit_cast(u32x2, a);
+    const u32x2 b2 = __builtin_bit_cast(u32x2, b);
+    return u32x4{a2[0], a2[1], b2[0], b2[1]};
+}
+
+// Stage `rows` rows (of ROWS total in the tile; the rest zero) of a strided
+// bf16 matrix into a swizzled LDS tile, all 256 threads; two phases so the
+// loads can be in flight while the caller computes
+template <int D, int ROWS>
+struct Stage {
+    static constexpr int CHUNKS = ROWS * BCfg<D>::UNITS;   // 16-byte units
+    static constexpr int PER = CHUNKS / 256;
+    u32x4 r[PER];
+    __device__ __forceinline__ void load(const __bf16* base, long long stride, int rows, int tid) {
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+            const int c = tid + 256 * n;
+            const int row = c / BCfg<D>::UNITS, p = c % BCfg<D>::UNITS;
+            r[n] = row < rows ? *reinterpret_cast<const u32x4*>(base + row * stride + 8 * p)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void store(lds_char* t, int tid) const {
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+            const int c = tid + 256 * n;
+            const int row = c / BCfg<D>::UNITS, p = c % BCfg<D>::UNITS;
+            *(lds_u32x4*)(t + row * BCfg<D>::ROW_BYTES + 16 * (p ^ swz<D>(row))) = r[n];
+        }
+    }
+};
+
+// ---------------------------------------------------------------- delta
+template <int D>
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);   // over [B, Tq, Hq]
+    if (row >= (long long)a.B * a.Tq * a.Hq) return;
+    const __bf16* dO = static_cast<const __bf16*>(a.dout) + row * D + lane * PER;
+    const float* o = a.out + row * D + lane * PER;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) s += (float)dO[e] * o[e];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) {
+        const long long h = row % a.Hq, bi = row / a.Hq;
+        const long long i = bi % a.Tq, b = bi / a.Tq;
+        a.delta[(b * a.Hq + h) * a.Tq + i] = s;
+    }
+}
+
+// ---------------------------------------------------------------- dq
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
+    using C = BCfg<D>;
+    constexpr int KT = 64, TB = KT * C::ROW_BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];   // 2 x [K | V]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    const int bg = blockIdx.x / a.wg_per_bg, qt = blockIdx.x % a.wg_per_bg;
+    const int b = bg / a.Hkv, g = bg % a.Hkv, G = a.Hq / a.Hkv;
+    const int npblk = (a.Tq + 31) / 32;
+    const int task = qt * 4 + wave, pblk = task / G, h = g * G + task % G;
+    const bool wave_valid = pblk < npblk;
+    const int row = pblk * 32 + l32;
+    const bool row_ok = wave_valid && row < a.Tq;
+    int last_pblk = (qt * 4 + 3) / G;
+    if (last_pblk > npblk - 1) last_pblk = npblk - 1;
+    const long long wg_last_pos = a.q_off + min(a.Tq, (last_pblk + 1) * 32) - 1;
+    const long long qpos = a.q_off + row;
+    const long long q_rs = (long long)a.Hq * D, kv_rs = (long long)a.Hkv * D;
+
+    // Q^T and dO^T (B operands): lane (l32, hh) holds [row][16s + 8hh .. +7]
+    u32x4 qf[C::DSTEPS], df[C::DSTEPS];
+    {
+        const long long ro = ((long long)b * a.Tq + (row_ok ? row : 0)) * q_rs + (long long)h * D;
+        const __bf16* qb = static_cast<const __bf16*>(a.q) + ro;
+        const __bf16* db_ = static_cast<const __bf16*>(a.dout) + ro;
+#pragma unroll
+        for (int s = 0; s < C::DSTEPS; ++s) {
+            qf[s] = row_ok ? *reinterpret_cast<const u32x4*>(qb + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+            df[s] = row_ok ? *reinterpret_cast<const u32x4*>(db_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // this row's lse (log2 units) and delta; rows without any key or past
+    // the end get p = 0 (lse2 = +inf)
+    float lse2 = INFINITY, dlt = 0.f;
+    if (row_ok) {
+        const long long si = ((long long)b * a.Hq + h) * a.Tq + row;
+        const float l = a.lse[si];
+        lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+        dlt = a.delta[si];
+    }
+    f32x16 dq_acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq_acc[db][r] = 0.f;
+
+    // tiles: blocks in order, 64 keys at a time, only keys at or before the
+    // workgroup's last query (causal)
+    auto need = [&](int t) -> int {
+        const int len = a.kv_len[t];
+        if (!a.causal) return len;
+        const long long n = wg_last_pos - a.kv_off[t] + 1;
+        return n <= 0 ? 0 : (n < len ? (int)n : len);
+    };
+    int bi = 0, ti = 0;
+    while (bi < a.n_blocks && need(bi) == 0) ++bi;
+    Stage<D, KT> sk, sv;
+    auto load_tile = [&](int blk, int tile) {
+        const int key0 = tile * KT;
+        const int rows = min(KT, a.kv_len[blk] - key0);
+        const long long base = ((long long)b * a.kv_len[blk] + key0) * kv_rs + (long long)g * D;
+        sk.load(static_cast<const __bf16*>(a.k[blk]) + base, kv_rs, rows, tid);
+        sv.load(static_cast<const __bf16*>(a.v[blk]) + base, kv_rs, rows, tid);
+    };
+    auto advance = [&](int& blk, int& tile) {
+        if (++tile * KT >= need(blk)) {
+            tile = 0;
+            ++blk;
+            while (blk < a.n_blocks && need(blk) == 0) ++blk;
+        }
+    };
+    int buf = 0;
+    if (bi < a.n_blocks) {
+        load_tile(bi, ti);
+        sk.store((lds_char*)smem, tid);
+        sv.store((lds_char*)smem + TB, tid);
+    }
+    __syncthreads();
+    while (bi < a.n_blocks) {
+        int nbi = bi, nti = ti;
+        advance(nbi, nti);
+        if (nbi < a.n_blocks) load_tile(nbi, nti);
+        const lds_char* kt = (const lds_char*)smem + buf * 2 * TB;
+        const lds_char* vt = kt + TB;
+        const int key0 = ti * KT;
+        const int tile_keys = min(KT, a.kv_len[bi] - key0);
+        const long long kpos0 = a.kv_off[bi] + key0;
+        if (wave_valid) {
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    s[kb][r] = 0.f;
+                    dp[kb][r] = 0.f;
+                }
+            // S^T = K Q^T, dP^T = V dO^T: s[kb][r] = score(row, key 32kb + 16hh + r)
+#pragma unroll
+            for (int f = 0; f < 2 * C::DSTEPS; ++f) {
+                const int st = f / 2, kb = f % 2;
+                const int krow = 32 * kb + perm_row(l32);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_unit<D>(kt, krow, 2 * st + hh)), as_bf16x8(qf[st]), s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_unit<D>(vt, krow, 2 * st + hh)), as_bf16x8(df[st]), dp[kb], 0, 0, 0);
+            }
+            // P and dS = P (dP - delta); keys past the tile or (causal) after
+            // this row get p = 0
+            const long long dq64 = qpos - kpos0;
+            const int dqp = dq64 > (1 << 30) ? (1 << 30) : (dq64 < -(1 << 30) ? -(1 << 30) : (int)dq64);
+            u32x4 dsb[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int run0 = 32 * kb + 16 * hh;
+                int lim = tile_keys - 1 - run0;
+                if (a.causal) lim = min(lim, dqp - run0);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x8 d8;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int r = 8 * j + u;
+                        const float p = r <= lim ? fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2)) : 0.f;
+                        d8[u] = p * (dp[kb][r] - dlt);
+                    }
+                    dsb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
+                }
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int f = 0; f < 4 * C::DB; ++f) {
+                const int db = f % C::DB, j = (f / C::DB) % 2, kb = f / (2 * C::DB);
+                dq_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_tr<D>(kt + kb * 32 * C::ROW_BYTES, lane, j, db)),
+                    as_bf16x8(dsb[kb][j]), dq_acc[db], 0, 0, 0);
+            }
+        }
+        if (nbi < a.n_blocks) {
+            lds_char* nk = (lds_char*)smem + (buf ^ 1) * 2 * TB;
+            sk.store(nk, tid);
+            sv.store(nk + TB, tid);
+        }
+        __syncthreads();
+        bi = nbi;
+        ti = nti;
+        buf ^= 1;
+    }
+    if (row_ok) {
+        float* dq = a.dq + (((long long)b * a.Tq + row) * a.Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                f32x4 x;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) x[jj] = dq_acc[db][4 * ib + jj] * a.scale;
+                *reinterpret_cast<f32x4*>(dq + 32 * db + 8 * ib + 4 * hh) = x;
+            }
+    }
+}
+
+// ---------------------------------------------------------------- dk, dv
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
+    using C = BCfg<D>;
+    constexpr int QR = 32, TB = QR * C::ROW_BYTES;
+    // 2 x [Q | dO | lse2[32] | delta[32]]
+    constexpr int BUF = 2 * TB + 2 * QR * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    const int ntiles = a.kt0[a.n_blocks];
+    int id = blockIdx.x;
+    const int kt = id % ntiles;
+    id /= ntiles;
+    const int g = id % a.Hkv, b = id / a.Hkv, G = a.Hq / a.Hkv;
+    int blk = 0;
+    while (blk + 1 < a.n_blocks && a.kt0[blk + 1] <= kt) ++blk;
+    const int len = a.kv_len[blk];
+    const int wkey0 = (kt - a.kt0[blk]) * kBwdKeyTile;   // the workgroup's first key
+    const int key = wkey0 + 32 * wave + l32;              // this lane's key
+    const bool key_ok = key < len;
+    const long long kpos = a.kv_off[blk] + key;
+    const long long wg_first_kpos = a.kv_off[blk] + wkey0;
+    const long long q_rs = (long long)a.Hq * D, kv_rs = (long long)a.Hkv * D;
+
+    // K^T and V^T (B operands): lane (l32 = key, hh) holds [key][16s + 8hh .. +7]
+    u32x4 kf[C::DSTEPS], vf[C::DSTEPS];
+    {
+        const long long ko = ((long long)b * len + (key_ok ? key : 0)) * kv_rs + (long long)g * D;
+        const __bf16* kb_ = static_cast<const __bf16*>(a.k[blk]) + ko;
+        const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) + ko;
+#pragma unroll
+        for (int s = 0; s < C::DSTEPS; ++s) {
+            kf[s] = key_ok ? *reinterpret_cast<const u32x4*>(kb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+            vf[s] = key_ok ? *reinterpret_cast<const u32x4*>(vb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    f32x16 dk_acc[C::DB], dv_acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dk_acc[db][r] = 0.f;
+            dv_acc[db][r] = 0.f;
+        }
+
+    // query tiles: (head j of the group, 32-row block), skipping blocks whose
+    // last row comes before the workgroup's first key (causal)
+    const int nrt = (a.Tq + QR - 1) / QR;
+    auto tile_ok = [&](int rt) -> bool {
+        return !a.causal || a.q_off + min(a.Tq, (rt + 1) * QR) - 1 >= wg_first_kpos;
+    };
+    int rt0 = 0;
+    while (rt0 < nrt && !tile_ok(rt0)) ++rt0;
+    const int nq = (nrt - rt0) * G;   // query tiles to visit: (head, row block)
+    Stage<D, QR> sq, sd;
+    float ls = 0.f, dl = 0.f;
+    auto load_tile = [&](int n) {
+        const int hj = n % G, rt = rt0 + n / G;
+        const int h = g * G + hj;
+        const int r0 = rt * QR, rows = min(QR, a.Tq - r0);
+        const long long base = ((long long)b * a.Tq + r0) * q_rs + (long long)h * D;
+        sq.load(static_cast<const __bf16*>(a.q) + base, q_rs, rows, tid);
+        sd.load(static_cast<const __bf16*>(a.dout) + base, q_rs, rows, tid);
+        if (tid < QR) {
+            const long long si = ((long long)b * a.Hq + h) * a.Tq + r0 + tid;
+            const float l = tid < rows ? a.lse[si] : -INFINITY;
+            ls = l == -INFINITY ? INFINITY : l * kLog2e;
+            dl = tid < rows ? a.delta[si] : 0.f;
+        }
+    };
+    auto store_tile = [&](lds_char* t) {
+        sq.store(t, tid);
+        sd.store(t + TB, tid);
+        if (tid < QR) {
+            ((__attribute__((address_space(3))) float*)(t + 2 * TB))[tid] = ls;
+            ((__attribute__((address_space(3))) float*)(t + 2 * TB + QR * 4))[tid] = dl;
+        }
+    };
+    if (nq > 0) {
+        load_tile(0);
+        store_tile((lds_char*)smem);
+    }
+    __syncthreads();
+    for (int n = 0; n < nq; ++n) {
+        const int buf = n & 1;
+        if (n + 1 < nq) load_tile(n + 1);
+        const lds_char* qt = (const lds_char*)smem + buf * BUF;
+        const lds_char* dt = qt + TB;
+        const int r0 = (rt0 + n / G) * QR;
+        {
+            // S = Q K^T, dP = dO V^T: s[r] = score(row r0 + 16hh + r, key)
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[r] = 0.f;
+                dp[r] = 0.f;
+            }
+#pragma unroll
+            for (int st = 0; st < C::DSTEPS; ++st) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_unit<D>(qt, perm_row(l32), 2 * st + hh)), as_bf16x8(kf[st]), s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_unit<D>(dt, perm_row(l32), 2 * st + hh)), as_bf16x8(vf[st]), dp, 0, 0, 0);
+            }
+            // per-row lse2 and delta of rows 16hh .. 16hh+15 (same for every lane of a half)
+            f32x16 lr, dr;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 l4 = *(const lds_f32x4*)(qt + 2 * TB + 4 * (16 * hh + 4 * q4));
+                const f32x4 d4 = *(const lds_f32x4*)(qt + 2 * TB + QR * 4 + 4 * (16 * hh + 4 * q4));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lr[4 * q4 + e] = l4[e];
+                    dr[4 * q4 + e] = d4[e];
+                }
+            }
+            // allowed: key present and (causal) at or before the row's position
+            const long long d64 = a.q_off + r0 + 16 * hh - kpos;   // row position minus key position at r = 0
+            const int dlo = d64 > (1 << 30) ? (1 << 30) : (d64 < -(1 << 30) ? -(1 << 30) : (int)d64);
+            u32x4 pb[2], dsb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x8 p8, d8;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int r = 8 * j + u;
+                    const bool ok = key_ok && (!a.causal || r + dlo >= 0);
+                    const float p = ok ? fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lr[r])) : 0.f;
+                    p8[u] = p;
+                    d8[u] = p * (dp[r] - dr[r]);
+                }
+                pb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p8, bf16x8));
+                dsb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+            for (int f = 0; f < 2 * C::DB; ++f) {
+                const int db = f % C::DB, j = f / C::DB;
+                dv_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_tr<D>(dt, lane, j, db)), as_bf16x8(pb[j]), dv_acc[db], 0, 0, 0);
+                dk_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(tile_tr<D>(qt, lane, j, db)), as_bf16x8(dsb[j]), dk_acc[db], 0, 0, 0);
+            }
+        }
+        if (n + 1 < nq) store_tile((lds_char*)smem + (buf ^ 1) * BUF);
+        __syncthreads();
+    }
+    if (key_ok) {
+        const long long ko = (((long long)b * len + key) * a.Hkv + g) * D;
+        float* dk = a.dk[blk] + ko;
+        float* dv = a.dv[blk] + ko;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                f32x4 xk, xv;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    xk[jj] = dk_acc[db][4 * ib + jj] * a.scale;
+                    xv[jj] = dv_acc[db][4 * ib + jj];
+                }
+                *reinterpret_cast<f32x4*>(dk + 32 * db + 8 * ib + 4 * hh) = xk;
+                *reinterpret_cast<f32x4*>(dv + 32 * db + 8 * ib + 4 * hh) = xv;
+            }
+    }
+}
+
+template <int D>
+int launch_all(const BwdArgs& a, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const long long rows = (long long)a.B * a.Tq * a.Hq;
+    const long long n_dq = (long long)a.B * a.Hkv * a.wg_per_bg;
+    const long long n_kv = (long long)a.B * a.Hkv * a.kt0[a.n_blocks];
+    if (rows > 0) {
+        hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    if (n_dq > 0) {
+        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(256), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    if (n_kv > 0) {
+        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_kv), dim3(256), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return (int)hipSuccess;
+}
+
+}  // namespace
+
+int launch_bwd(const BwdArgs& a, int D, void* stream) {
+    if (D == 128) return launch_all<128>(a, stream);
+    if (D == 64) return launch_all<64>(a, stream);
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace cakv

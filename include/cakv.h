@@ -222,6 +222,42 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
                                 int64_t* tile_counters, void* stream);
 
 /*
+ * Gradients of cakv_forward_blocks for training (the pages apply sequence
+ * parallelism to training as well as inference, section "Training and
+ * inference stress this dimension differently", but give no backward
+ * formulas): the chain rule through the definition of section "Attention
+ * wants keys and values from other tokens", with p = e^{s - lse}
+ * recomputed from the forward's lse:
+ *   delta_i = dout_i . out_i,  ds_ij = p_ij (dout_i . v_j - delta_i),
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dout_i   (grouped query heads add into their kv head).
+ * q, k_blocks, v_blocks, kv_len, kv_off, q_offset, causal, scale: exactly as
+ *   given to the forward (bf16 only);
+ * out: [B, Tq, Hq, D] fp32 and lse: [B, Hq, Tq] fp32 from that forward;
+ * dout: [B, Tq, Hq, D] bf16, the gradient of the loss with respect to out;
+ * dq: [B, Tq, Hq, D] fp32; dk_blocks_host, dv_blocks_host: HOST arrays of
+ *   device pointers, block t = [B, kv_len_host[t], Hkv, D] fp32. All outputs
+ *   are overwritten (a block no query sees gets zeros).
+ * workspace: device buffer of cakv_backward_workspace_size bytes (the
+ *   per-row delta), 16-byte aligned, owned by the caller.
+ * Errors: CAKV_ERR_DTYPE unless dtype = CAKV_BF16; otherwise as for
+ * cakv_forward_blocks, plus NULL out / lse / dout / dq / gradient block
+ * pointers and a too small workspace (CAKV_ERR_SHAPE).
+ */
+cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host,
+                                 const void* const* v_blocks_host, const int64_t* kv_len_host,
+                                 const int64_t* kv_off_host, int n_blocks, int dtype, int B,
+                                 int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
+                                 float scale, const float* out, const float* lse,
+                                 const void* dout, float* dq, float* const* dk_blocks_host,
+                                 float* const* dv_blocks_host, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace cakv_backward_blocks needs (B * Hq * Tq * 4), written
+ * to the HOST int64 *bytes_host. */
+cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host);
+
+/*
  * Decode over a KV history held in portions (page section "Training and
  * inference stress this dimension differently": during inference each device
  * holds one portion of a long conversation's keys and values, the new query

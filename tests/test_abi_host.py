@@ -253,3 +253,26 @@ def test_forward_blocks_errors():
     assert fb(k=None) == 1
     assert fb(q=MIS) == 4
     assert fb(B=0, q=None, out=None) == 0
+
+
+def test_backward_errors():
+    I64 = ctypes.c_int64
+    lens = (I64 * 1)(100)
+    offs = (I64 * 1)(0)
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    nb = I64(0)
+    assert L.cakv_backward_workspace_size(2, 8, 300, ctypes.byref(nb)) == 0 and nb.value == 2 * 8 * 300 * 4
+    assert L.cakv_backward_workspace_size(-1, 8, 300, ctypes.byref(nb)) == 2
+
+    def bw(dtype=1, n=1, D=128, q=FAKE, dout=FAKE, ws=FAKE, wsb=8 * 50 * 4, dk=ptrs):
+        return L.cakv_backward_blocks(q, ptrs, ptrs, lens, offs, n, dtype, 1, 8, 2, 50, D, 100, 1,
+                                      0.0, FAKE, FAKE, dout, FAKE, dk, ptrs, ws, wsb, None)
+    assert bw(dtype=0) == 3
+    assert bw(n=0) == 5
+    assert bw(D=96) == 2
+    assert bw(q=None) == 1
+    assert bw(dout=None) == 1
+    assert bw(dk=None) == 1
+    assert bw(ws=None) == 1
+    assert bw(wsb=16) == 2
+    assert bw(q=MIS) == 4

@@ -1,0 +1,93 @@
+"""GPU parity of cakv_backward_blocks against the fp64 gradient oracle (O4).
+
+The GPU side runs the forward (cakv_forward_blocks: out fp32, lse) and then
+the backward on the same seeded bf16 inputs and a seeded bf16 upstream
+gradient dout; the oracle differentiates the plain definition in fp64 on the
+same stored values.
+
+Tolerance, per gradient tensor, relative to the reference's scale
+(rms = root-mean-square of the reference tensor): max |d| <= 5e-2 * rms' and
+mean |d| <= 4e-3 * rms', rms' = max(rms, 1e-3). The kernels round p and ds to
+bf16 (relative error up to 2^-9 ~ 2e-3, rms ~1.1e-3) before the products that
+sum them over keys or rows, so a gradient entry's error is ~1e-3 of the rms of
+its terms (measured: mean |d| ~1.3e-3 rms); the largest of ~10^5 entries
+lands about 20 times higher (measured up to 2.3e-2 rms), hence the max bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import cakv_synth as syn
+import context_attention_kv_amd as cakv
+import oracle
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _seq(B, Hq, Hkv, T, D, seed):
+    w = syn.Workload("backward", B=B, Hq=Hq, Hkv=Hkv, T=T, N=1, D=D, dtype="bf16",
+                     causal=True, ranks=(0,), seed=seed)
+    q = syn.make_q_full(w)
+    k = syn.make_kv_full(w, "k")
+    v = syn.make_kv_full(w, "v")
+    dout = np.empty((B, T, Hq, D), np.uint16)
+    syn.fill(dout, seed=seed, tensor=7)
+    return q, k, v, dout
+
+
+def _check(name, got, ref):
+    d = np.abs(got.astype(np.float64) - ref)
+    rms = max(float(np.sqrt((ref ** 2).mean())), 1e-3)
+    st = dict(max=float(d.max()), mean=float(d.mean()), rms_ref=rms)
+    say(f"  {name}: {st}")
+    assert not np.isnan(got).any(), name
+    assert st["max"] <= 5e-2 * rms, (name, st)
+    assert st["mean"] <= 4e-3 * rms, (name, st)
+
+
+def _run(q, k, v, dout, blocks, q_off, causal):
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(dout)
+    kb = [kd[:, o:o + l].contiguous() for o, l in blocks]
+    vb = [vd[:, o:o + l].contiguous() for o, l in blocks]
+    offs = [o for o, _ in blocks]
+    B, Tq, Hq, D = q.shape
+    out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+    cakv.cakv_forward_blocks(qd, kb, vb, offs, q_off, causal, out, lse)
+    dq = torch.full((B, Tq, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    dk = [torch.full(t.shape, float("nan"), dtype=torch.float32, device="cuda") for t in kb]
+    dv = [torch.full(t.shape, float("nan"), dtype=torch.float32, device="cuda") for t in kb]
+    cakv.cakv_backward_blocks(qd, kb, vb, offs, q_off, causal, out, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), [t.cpu().numpy() for t in dk], [t.cpu().numpy() for t in dv]
+
+
+def test_backward_causal_diagonal_and_future_block():
+    q, k, v, dout = _seq(2, 8, 2, 700, 128, 4001)
+    q_off, Tq = 300, 300
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    ds = np.ascontiguousarray(dout[:, q_off:q_off + Tq])
+    blocks = [(300, 300), (0, 300), (600, 100)]   # diagonal, full, wholly in the future
+    say(f"backward causal blocks={blocks}")
+    dq, dk, dv = _run(qs, k, v, ds, blocks, q_off, True)
+    rq, rk, rv = oracle.attention_backward(qs, k, v, ds, q_off=q_off, k_off=0, causal=True)
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
+    assert not dk[2].any() and not dv[2].any()
+
+
+def test_backward_bidirectional_unequal_blocks_d64_gqa():
+    q, k, v, dout = _seq(1, 12, 3, 900, 64, 4002)
+    q_off, Tq = 100, 257
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    ds = np.ascontiguousarray(dout[:, q_off:q_off + Tq])
+    blocks = [(500, 400), (0, 130), (130, 370)]
+    dq, dk, dv = _run(qs, k, v, ds, blocks, q_off, False)
+    rq, rk, rv = oracle.attention_backward(qs, k, v, ds, q_off=q_off, k_off=0, causal=False)
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
