@@ -257,6 +257,14 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_unit<D>(vt, krow, 2 * st + hh)), as_bf16x8(df[st]), dp[kb], 0, 0, 0);
             }
+            // pipeline: four operand reads ahead, then one read per product
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int f = 0; f < 4 * C::DSTEPS - 4; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             // P and dS = P (dP - delta); keys past the tile or (causal) after
             // this row get p = 0
             const long long dq64 = qpos - kpos0;
@@ -287,6 +295,13 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
                     as_bf16x8(tile_tr<D>(kt + kb * 32 * C::ROW_BYTES, lane, j, db)),
                     as_bf16x8(dsb[kb][j]), dq_acc[db], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int f = 0; f < 4 * C::DB - 4; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         if (nbi < a.n_blocks) {
             lds_char* nk = (lds_char*)smem + (buf ^ 1) * 2 * TB;
@@ -419,6 +434,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_unit<D>(dt, perm_row(l32), 2 * st + hh)), as_bf16x8(vf[st]), dp, 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int f = 0; f < 2 * C::DSTEPS - 4; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             // per-row lse2 and delta of rows 16hh .. 16hh+15 (same for every lane of a half)
             f32x16 lr, dr;
 #pragma unroll
@@ -458,6 +480,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
                 dk_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_tr<D>(qt, lane, j, db)), as_bf16x8(dsb[j]), dk_acc[db], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int f = 0; f < 4 * C::DB - 4; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         if (n + 1 < nq) store_tile((lds_char*)smem + (buf ^ 1) * BUF);
         __syncthreads();
