@@ -251,24 +251,33 @@ int oracle_classify(int64_t Tq, int64_t q_off, int64_t k_off, int causal,
         return -1;
     int64_t tc[3] = {0, 0, 0};
     for (int64_t t = 0; t < n_blocks; ++t) {
-        int64_t pairs = 0;
-        for (int64_t i = 0; i < Tq; ++i)
-            for (int64_t j = starts[t]; j < starts[t] + lens[t]; ++j)
-                pairs += allowed(causal, k_off + j, q_off + i);
-        const int64_t total = Tq * lens[t];
-        if (block_class)
-            block_class[t] = (pairs == 0) ? 2 : (pairs == total ? 0 : 1);
-        if (pairs_out) pairs_out[t] = pairs;
-        for (int64_t i0 = 0; i0 < Tq; i0 += tile_q)
+        /* every pair is counted once, inside its tile; the block's count is
+           the sum over its tiles (row tiles spread over threads) */
+        int64_t pairs = 0, n_full = 0, n_part = 0, n_skip = 0;
+        const int64_t n_row_tiles = (Tq + tile_q - 1) / tile_q;
+#pragma omp parallel for schedule(dynamic, 1) reduction(+ : pairs, n_full, n_part, n_skip)
+        for (int64_t it = 0; it < n_row_tiles; ++it) {
+            const int64_t i0 = it * tile_q;
+            const int64_t i1 = i0 + tile_q < Tq ? i0 + tile_q : Tq;
             for (int64_t j0 = 0; j0 < lens[t]; j0 += tile_k) {
-                const int64_t i1 = i0 + tile_q < Tq ? i0 + tile_q : Tq;
                 const int64_t j1 = j0 + tile_k < lens[t] ? j0 + tile_k : lens[t];
                 int64_t p = 0;
                 for (int64_t i = i0; i < i1; ++i)
                     for (int64_t j = j0; j < j1; ++j)
                         p += allowed(causal, k_off + starts[t] + j, q_off + i);
-                tc[(p == 0) ? 2 : (p == (i1 - i0) * (j1 - j0) ? 0 : 1)] += 1;
+                pairs += p;
+                if (p == 0) ++n_skip;
+                else if (p == (i1 - i0) * (j1 - j0)) ++n_full;
+                else ++n_part;
             }
+        }
+        const int64_t total = Tq * lens[t];
+        if (block_class)
+            block_class[t] = (pairs == 0) ? 2 : (pairs == total ? 0 : 1);
+        if (pairs_out) pairs_out[t] = pairs;
+        tc[0] += n_full;
+        tc[1] += n_part;
+        tc[2] += n_skip;
     }
     if (tile_counts)
         for (int c = 0; c < 3; ++c) tile_counts[c] = tc[c] * B * Hq;
