@@ -15,15 +15,20 @@
 // bwd_delta_kernel: delta per query row (one wave per row).
 // bwd_dq_kernel: query-stationary, 4 waves per workgroup, each wave 32 rows of
 //   one query head (grouped heads share the workgroup's K/V tiles). Per
-//   64-key tile, staged in LDS through registers (double buffer):
+//   64-key tile, copied from HBM straight into LDS (double buffer):
 //   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 (K, V as A
 //   operands, Q^T and dO^T in registers as B), dS = P (dP - delta), then
 //   dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16.
-// bwd_dkdv_kernel: key-stationary, 4 waves of 32 keys (K^T and V^T in
-//   registers as B operands) over every 32-row query tile of the kv head's
-//   query heads, staged in LDS: S = Q K^T and dP = dO V^T (query rows in
-//   output registers), dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
-//   read through ds_read_b64_tr_b16.
+// bwd_dkdv_kernel: key-stationary, 4 waves of 32 keys (K^T in registers and
+//   the workgroup's 128 V rows in LDS, both B operands) over every 32-row
+//   query tile of the kv head's query heads, copied into LDS: S = Q K^T and
+//   dP = dO V^T (query rows in output registers), dV^T += dO^T P and
+//   dK^T += Q^T dS with dO^T and Q^T read through ds_read_b64_tr_b16.
+// Both kernels fit two waves per SIMD (two workgroups per CU), so one
+// workgroup's products overlap the other's softmax work and barrier waits.
+// Tile copies use buffer loads that write LDS directly: no staging registers,
+// and the range check of a per-tile buffer resource zero-fills rows past the
+// end of a block or of the query range.
 #include <hip/hip_runtime.h>
 
 #include "bwd_args.h"
@@ -39,6 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -99,32 +105,55 @@ __device__ __forceinline__ u32x4 tile_tr(const lds_char* t, int lane, int j, int
     return u32x4{a2[0], a2[1], b2[0], b2[1]};
 }
 
-// Stage `rows` rows (of ROWS total in the tile; the rest zero) of a strided
-// bf16 matrix into a swizzled LDS tile, all 256 threads; two phases so the
-// loads can be in flight while the caller computes
-template <int D, int ROWS>
-struct Stage {
-    static constexpr int CHUNKS = ROWS * BCfg<D>::UNITS;   // 16-byte units
-    static constexpr int PER = CHUNKS / 256;
-    u32x4 r[PER];
-    __device__ __forceinline__ void load(const __bf16* base, long long stride, int rows, int tid) {
-#pragma unroll
-        for (int n = 0; n < PER; ++n) {
-            const int c = tid + 256 * n;
-            const int row = c / BCfg<D>::UNITS, p = c % BCfg<D>::UNITS;
-            r[n] = row < rows ? *reinterpret_cast<const u32x4*>(base + row * stride + 8 * p)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-    __device__ __forceinline__ void store(lds_char* t, int tid) const {
-#pragma unroll
-        for (int n = 0; n < PER; ++n) {
-            const int c = tid + 256 * n;
-            const int row = c / BCfg<D>::UNITS, p = c % BCfg<D>::UNITS;
-            *(lds_u32x4*)(t + row * BCfg<D>::ROW_BYTES + 16 * (p ^ swz<D>(row))) = r[n];
-        }
-    }
-};
+// Buffer resource of `bytes` bytes at `base` (raw: stride 0, 32-bit data
+// format). Lanes whose offset falls at or past `bytes` read zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+    i32x4 r;
+    r[0] = (int)(unsigned)p;
+    r[1] = (int)((p >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = 0x00020000;
+    return r;
+}
+// Buffer -> LDS copies: lane i's 16 (4) bytes from byte offset voff of the
+// resource land at LDS address lds_base + 16 i (+ 4 i). Inline assembly, so
+// that the compiler does not wait for them before unrelated LDS reads; the
+// issuing wave waits for them (wait_vmem) before the barrier that publishes
+// the tile.
+__device__ __forceinline__ void copy16_to_lds(i32x4 rsrc, unsigned voff, unsigned lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds_base)
+        : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(i32x4 rsrc, unsigned voff, unsigned lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %0, %1, 0 offen lds"
+        :
+        : "v"(voff), "s"(rsrc), "s"(lds_base)
+        : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Lane-constant byte offset of copy region `lr` (1 KB of a swizzled tile of
+// rows of `rs` elements): this lane fetches 16-byte unit p of tile row `row`
+// such that it lands at its swizzled place.
+template <int D>
+__device__ __forceinline__ unsigned region_off(int lr, int lane, long long rs) {
+    constexpr int RPK = 1024 / BCfg<D>::ROW_BYTES;   // rows per 1 KB region
+    const int row = lr * RPK + lane / BCfg<D>::UNITS;
+    const int p = lane % BCfg<D>::UNITS;
+    return (unsigned)(2 * (row * rs + 8 * (p ^ swz<D>(row))));
+}
 
 // ---------------------------------------------------------------- delta
 template <int D>
@@ -149,10 +178,12 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dq
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
     using C = BCfg<D>;
     constexpr int KT = 64, TB = KT * C::ROW_BYTES;
+    constexpr int NCP = TB / 1024 / 4;   // copies per wave per K (or V) tile
     __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TB];   // 2 x [K | V]
+    const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
@@ -207,13 +238,22 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
     };
     int bi = 0, ti = 0;
     while (bi < a.n_blocks && need(bi) == 0) ++bi;
-    Stage<D, KT> sk, sv;
-    auto load_tile = [&](int blk, int tile) {
+    // copy n of this wave fills 1 KB region 4n + wave of the K and of the V tile
+    unsigned cp_off[NCP];
+#pragma unroll
+    for (int n = 0; n < NCP; ++n) cp_off[n] = region_off<D>(4 * n + wave, lane, kv_rs);
+    auto issue = [&](int blk, int tile, unsigned dst) {
         const int key0 = tile * KT;
         const int rows = min(KT, a.kv_len[blk] - key0);
         const long long base = ((long long)b * a.kv_len[blk] + key0) * kv_rs + (long long)g * D;
-        sk.load(static_cast<const __bf16*>(a.k[blk]) + base, kv_rs, rows, tid);
-        sv.load(static_cast<const __bf16*>(a.v[blk]) + base, kv_rs, rows, tid);
+        const unsigned bytes = (unsigned)(rows * kv_rs * 2);
+        const i32x4 rk = make_rsrc(static_cast<const __bf16*>(a.k[blk]) + base, bytes);
+        const i32x4 rv = make_rsrc(static_cast<const __bf16*>(a.v[blk]) + base, bytes);
+#pragma unroll
+        for (int n = 0; n < NCP; ++n) {
+            copy16_to_lds(rk, cp_off[n], dst + (4 * n + wave) * 1024);
+            copy16_to_lds(rv, cp_off[n], dst + TB + (4 * n + wave) * 1024);
+        }
     };
     auto advance = [&](int& blk, int& tile) {
         if (++tile * KT >= need(blk)) {
@@ -222,17 +262,20 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
             while (blk < a.n_blocks && need(blk) == 0) ++blk;
         }
     };
+    // the Q, dO, lse and delta loads above, in a form the compiler's wait
+    // tracking sees, so that no wait for them lands in the loop (where it
+    // would also wait for the tile copies in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     int buf = 0;
-    if (bi < a.n_blocks) {
-        load_tile(bi, ti);
-        sk.store((lds_char*)smem, tid);
-        sv.store((lds_char*)smem + TB, tid);
-    }
+    if (bi < a.n_blocks) issue(bi, ti, lds0);
+    wait_vmem<0>();
     __syncthreads();
     while (bi < a.n_blocks) {
         int nbi = bi, nti = ti;
         advance(nbi, nti);
-        if (nbi < a.n_blocks) load_tile(nbi, nti);
+        // the other buffer was last read before the barrier that ended the
+        // previous step
+        if (nbi < a.n_blocks) issue(nbi, nti, lds0 + (buf ^ 1) * 2 * TB);
         const lds_char* kt = (const lds_char*)smem + buf * 2 * TB;
         const lds_char* vt = kt + TB;
         const int key0 = ti * KT;
@@ -303,11 +346,7 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
-        if (nbi < a.n_blocks) {
-            lds_char* nk = (lds_char*)smem + (buf ^ 1) * 2 * TB;
-            sk.store(nk, tid);
-            sv.store(nk + TB, tid);
-        }
+        wait_vmem<0>();
         __syncthreads();
         bi = nbi;
         ti = nti;
@@ -329,12 +368,15 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dk, dv
 template <int D>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     using C = BCfg<D>;
     constexpr int QR = 32, TB = QR * C::ROW_BYTES;
-    // 2 x [Q | dO | lse2[32] | delta[32]]
-    constexpr int BUF = 2 * TB + 2 * QR * 4;
-    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+    constexpr int NCP = TB / 1024 / 4;            // copies per wave per Q (or dO) tile
+    constexpr int VT = kBwdKeyTile * C::ROW_BYTES;   // the workgroup's V rows
+    // [V rows] then 2 x [Q | dO | lse (64 floats) | delta (64 floats) | pad]
+    constexpr int BUF = 2 * TB + 1024;
+    __shared__ __attribute__((aligned(1024))) char smem[VT + 2 * BUF];
+    const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
@@ -348,22 +390,38 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     while (blk + 1 < a.n_blocks && a.kt0[blk + 1] <= kt) ++blk;
     const int len = a.kv_len[blk];
     const int wkey0 = (kt - a.kt0[blk]) * kBwdKeyTile;   // the workgroup's first key
-    const int key = wkey0 + 32 * wave + l32;              // this lane's key
+    // this lane's key: keys of the wave in the permuted order of the A-operand
+    // rows, so that the V rows it reads from LDS as a B operand are free of
+    // bank conflicts like the A reads (the order is the same everywhere: K^T,
+    // V^T, the mask and the dK, dV rows written)
+    const int wkey = 32 * wave + perm_row(l32);          // key within the workgroup's tile
+    const int key = wkey0 + wkey;
     const bool key_ok = key < len;
-    const long long kpos = a.kv_off[blk] + key;
     const long long wg_first_kpos = a.kv_off[blk] + wkey0;
+    const int lane_rel = 16 * hh - wkey;   // row 16hh of a tile minus this lane's key, relative
     const long long q_rs = (long long)a.Hq * D, kv_rs = (long long)a.Hkv * D;
 
-    // K^T and V^T (B operands): lane (l32 = key, hh) holds [key][16s + 8hh .. +7]
-    u32x4 kf[C::DSTEPS], vf[C::DSTEPS];
+    // K^T (B operand): lane (l32, hh) holds K[key][16s + 8hh .. +7]
+    u32x4 kf[C::DSTEPS];
     {
         const long long ko = ((long long)b * len + (key_ok ? key : 0)) * kv_rs + (long long)g * D;
         const __bf16* kb_ = static_cast<const __bf16*>(a.k[blk]) + ko;
-        const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) + ko;
 #pragma unroll
-        for (int s = 0; s < C::DSTEPS; ++s) {
+        for (int s = 0; s < C::DSTEPS; ++s)
             kf[s] = key_ok ? *reinterpret_cast<const u32x4*>(kb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
-            vf[s] = key_ok ? *reinterpret_cast<const u32x4*>(vb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // the workgroup's V rows into LDS (swizzled tile; rows past the block's end zero)
+    {
+        constexpr int PER = kBwdKeyTile * C::UNITS / 256;
+        const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) +
+                            ((long long)b * len + wkey0) * kv_rs + (long long)g * D;
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+            const int c = tid + 256 * n;
+            const int row = c / C::UNITS, p = c % C::UNITS;
+            const u32x4 x = wkey0 + row < len ? *reinterpret_cast<const u32x4*>(vb_ + row * kv_rs + 8 * p)
+                                              : u32x4{0u, 0u, 0u, 0u};
+            *(lds_u32x4*)((lds_char*)smem + row * C::ROW_BYTES + 16 * (p ^ swz<D>(row))) = x;
         }
     }
     f32x16 dk_acc[C::DB], dv_acc[C::DB];
@@ -384,39 +442,41 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
     int rt0 = 0;
     while (rt0 < nrt && !tile_ok(rt0)) ++rt0;
     const int nq = (nrt - rt0) * G;   // query tiles to visit: (head, row block)
-    Stage<D, QR> sq, sd;
-    float ls = 0.f, dl = 0.f;
-    auto load_tile = [&](int n) {
+    // copy n of this wave fills 1 KB region 4n + wave of the Q and of the dO
+    // tile; waves 0 and 1 also copy the tile's 32 lse and delta values
+    unsigned cp_off[NCP];
+#pragma unroll
+    for (int n = 0; n < NCP; ++n) cp_off[n] = region_off<D>(4 * n + wave, lane, q_rs);
+    auto issue = [&](int n, unsigned dst) {
         const int hj = n % G, rt = rt0 + n / G;
         const int h = g * G + hj;
         const int r0 = rt * QR, rows = min(QR, a.Tq - r0);
         const long long base = ((long long)b * a.Tq + r0) * q_rs + (long long)h * D;
-        sq.load(static_cast<const __bf16*>(a.q) + base, q_rs, rows, tid);
-        sd.load(static_cast<const __bf16*>(a.dout) + base, q_rs, rows, tid);
-        if (tid < QR) {
-            const long long si = ((long long)b * a.Hq + h) * a.Tq + r0 + tid;
-            const float l = tid < rows ? a.lse[si] : -INFINITY;
-            ls = l == -INFINITY ? INFINITY : l * kLog2e;
-            dl = tid < rows ? a.delta[si] : 0.f;
+        const unsigned bytes = (unsigned)(rows * q_rs * 2);
+        const i32x4 rq = make_rsrc(static_cast<const __bf16*>(a.q) + base, bytes);
+        const i32x4 rd = make_rsrc(static_cast<const __bf16*>(a.dout) + base, bytes);
+#pragma unroll
+        for (int c = 0; c < NCP; ++c) {
+            copy16_to_lds(rq, cp_off[c], dst + (4 * c + wave) * 1024);
+            copy16_to_lds(rd, cp_off[c], dst + TB + (4 * c + wave) * 1024);
+        }
+        if (wave < 2) {
+            const long long si = ((long long)b * a.Hq + h) * a.Tq + r0;
+            const i32x4 rs = make_rsrc(wave == 0 ? a.lse + si : a.delta + si, (unsigned)(rows * 4));
+            copy4_to_lds(rs, (unsigned)(4 * lane), dst + 2 * TB + 256 * wave);
         }
     };
-    auto store_tile = [&](lds_char* t) {
-        sq.store(t, tid);
-        sd.store(t + TB, tid);
-        if (tid < QR) {
-            ((__attribute__((address_space(3))) float*)(t + 2 * TB))[tid] = ls;
-            ((__attribute__((address_space(3))) float*)(t + 2 * TB + QR * 4))[tid] = dl;
-        }
-    };
-    if (nq > 0) {
-        load_tile(0);
-        store_tile((lds_char*)smem);
-    }
+    // the K and V loads above, in a form the compiler's wait tracking sees
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    if (nq > 0) issue(0, lds0 + VT);
+    wait_vmem<0>();
     __syncthreads();
     for (int n = 0; n < nq; ++n) {
         const int buf = n & 1;
-        if (n + 1 < nq) load_tile(n + 1);
-        const lds_char* qt = (const lds_char*)smem + buf * BUF;
+        // the other buffer was last read before the barrier that ended the
+        // previous step
+        if (n + 1 < nq) issue(n + 1, lds0 + VT + (buf ^ 1) * BUF);
+        const lds_char* qt = (const lds_char*)smem + VT + buf * BUF;
         const lds_char* dt = qt + TB;
         const int r0 = (rt0 + n / G) * QR;
         {
@@ -427,46 +487,52 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
                 s[r] = 0.f;
                 dp[r] = 0.f;
             }
+            const lds_char* vst = (const lds_char*)smem;
 #pragma unroll
             for (int st = 0; st < C::DSTEPS; ++st) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_unit<D>(qt, perm_row(l32), 2 * st + hh)), as_bf16x8(kf[st]), s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(tile_unit<D>(dt, perm_row(l32), 2 * st + hh)), as_bf16x8(vf[st]), dp, 0, 0, 0);
+                    as_bf16x8(tile_unit<D>(dt, perm_row(l32), 2 * st + hh)),
+                    as_bf16x8(tile_unit<D>(vst, wkey, 2 * st + hh)), dp, 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            // pipeline: one step's three operand reads ahead of its products
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-            for (int f = 0; f < 2 * C::DSTEPS - 4; ++f) {
+            for (int f = 0; f < C::DSTEPS - 1; ++f) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            // per-row lse2 and delta of rows 16hh .. 16hh+15 (same for every lane of a half)
-            f32x16 lr, dr;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 l4 = *(const lds_f32x4*)(qt + 2 * TB + 4 * (16 * hh + 4 * q4));
-                const f32x4 d4 = *(const lds_f32x4*)(qt + 2 * TB + QR * 4 + 4 * (16 * hh + 4 * q4));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lr[4 * q4 + e] = l4[e];
-                    dr[4 * q4 + e] = d4[e];
-                }
-            }
-            // allowed: key present and (causal) at or before the row's position
-            const long long d64 = a.q_off + r0 + 16 * hh - kpos;   // row position minus key position at r = 0
-            const int dlo = d64 > (1 << 30) ? (1 << 30) : (d64 < -(1 << 30) ? -(1 << 30) : (int)d64);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            // allowed: key present and (causal) at or before the row's
+            // position; dlo = position of row 16hh minus this lane's key
+            // (the tile's part is scalar, clamped to 32 bits)
+            const long long t64 = a.q_off + r0 - wg_first_kpos;
+            const int tq = t64 > (1 << 30) ? (1 << 30) : (t64 < -(1 << 30) ? -(1 << 30) : (int)t64);
+            const int dlo = tq + lane_rel;
             u32x4 pb[2], dsb[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
+                // lse (log2 units; a row without keys gets p = 0) and delta
+                // of rows 16hh + 8j .. +7 (the same for every lane of a half)
+                const int ro = 4 * (16 * hh + 8 * j);
+                const f32x4 l0 = *(const lds_f32x4*)(qt + 2 * TB + ro);
+                const f32x4 l1 = *(const lds_f32x4*)(qt + 2 * TB + ro + 16);
+                const f32x4 d0 = *(const lds_f32x4*)(qt + 2 * TB + 256 + ro);
+                const f32x4 d1 = *(const lds_f32x4*)(qt + 2 * TB + 256 + ro + 16);
                 f32x8 p8, d8;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int r = 8 * j + u;
+                    const float l = u < 4 ? l0[u] : l1[u - 4];
+                    const float dr = u < 4 ? d0[u] : d1[u - 4];
+                    const float l2 = l == -INFINITY ? INFINITY : l * kLog2e;
                     const bool ok = key_ok && (!a.causal || r + dlo >= 0);
-                    const float p = ok ? fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -lr[r])) : 0.f;
+                    const float p = ok ? fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l2)) : 0.f;
                     p8[u] = p;
-                    d8[u] = p * (dp[r] - dr[r]);
+                    d8[u] = p * (dp[r] - dr);
                 }
                 pb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p8, bf16x8));
                 dsb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
@@ -480,15 +546,16 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(const BwdArgs a) {
                 dk_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_tr<D>(qt, lane, j, db)), as_bf16x8(dsb[j]), dk_acc[db], 0, 0, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            // pipeline: two fragments read ahead of the products
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int f = 0; f < 4 * C::DB - 4; ++f) {
+            for (int f = 0; f < 4 * C::DB - 2; ++f) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
-        if (n + 1 < nq) store_tile((lds_char*)smem + (buf ^ 1) * BUF);
+        wait_vmem<0>();
         __syncthreads();
     }
     if (key_ok) {
