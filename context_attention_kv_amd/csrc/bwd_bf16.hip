@@ -31,6 +31,8 @@
 // end of a block or of the query range.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bwd_args.h"
 
 namespace cakv {
@@ -59,14 +61,21 @@ constexpr float kLog2e = 1.44269504088896341f;
 __device__ __forceinline__ int perm_row(int i) {
     return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
 }
-// XOR swizzle of the 16-byte units of a tile row (the forward kernel's
-// K-tile layout: conflict-free 16-byte operand reads)
+// XOR swizzle of the 16-byte units of a tile row. Every tile here is read
+// both ways: as A-operand rows (16-byte reads, rows perm_row(l32)) and through
+// the transposing 8-byte reads (four consecutive rows per 16-lane group). The
+// swizzle keeps both free of bank conflicts whether the LDS serves a 16-byte
+// read 8 lanes per cycle over 128 bytes or 16 lanes over 256 bytes, and an
+// 8-byte read 16 or 32 lanes per cycle: the row reads need it to be one-to-one
+// on row bits {0,1,2,4} (on {0,1,4} modulo 8), the transposing reads on row
+// bits {0,1} into unit bits {2,3} and {1,2}. (Unit bits for d = 128; for
+// d = 64 two rows share 256 bytes and the unit has three bits.)
 template <int D>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (D == 128)
-        return (row & 3) | (((row >> 4) & 1) << 2) | (((row >> 2) & 1) << 3);
+        return (row & 3) | (((row ^ (row >> 4)) & 1) << 2) | ((((row >> 1) ^ (row >> 2)) & 1) << 3);
     else
-        return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row ^ (row >> 2)) & 1) << 2);
+        return ((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1) | ((((row >> 1) ^ (row >> 4)) & 1) << 2);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -290,7 +299,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
                     s[kb][r] = 0.f;
                     dp[kb][r] = 0.f;
                 }
-            // S^T = K Q^T, dP^T = V dO^T: s[kb][r] = score(row, key 32kb + 16hh + r)
+            // S^T = K Q^T, dP^T = V dO^T: s[kb][r] = score(row, key 32kb + 16hh + r).
+            // Products issue at raised wave priority, so that on a SIMD shared
+            // with a wave in its vector phase they follow each other.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int f = 0; f < 2 * C::DSTEPS; ++f) {
                 const int st = f / 2, kb = f % 2;
@@ -308,29 +320,39 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_s_setprio(0);
             // P and dS = P (dP - delta); keys past the tile or (causal) after
             // this row get p = 0
             const long long dq64 = qpos - kpos0;
             const int dqp = dq64 > (1 << 30) ? (1 << 30) : (dq64 < -(1 << 30) ? -(1 << 30) : (int)dq64);
+            // every key of the tile visible to every row of the wave (wave-uniform)
+            const bool full = tile_keys == KT && (!a.causal || a.q_off + pblk * 32 - kpos0 >= KT - 1);
             u32x4 dsb[2][2];
+            auto scores_to_ds = [&](auto masked_c) {
+                constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int run0 = 32 * kb + 16 * hh;
-                int lim = tile_keys - 1 - run0;
-                if (a.causal) lim = min(lim, dqp - run0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int run0 = 32 * kb + 16 * hh;
+                    int lim = tile_keys - 1 - run0;
+                    if (a.causal) lim = min(lim, dqp - run0);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    f32x8 d8;
+                    for (int j = 0; j < 2; ++j) {
+                        f32x8 d8;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) {
-                        const int r = 8 * j + u;
-                        const float p = r <= lim ? fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2)) : 0.f;
-                        d8[u] = p * (dp[kb][r] - dlt);
+                        for (int u = 0; u < 8; ++u) {
+                            const int r = 8 * j + u;
+                            const float e = fast_exp2(__builtin_fmaf(s[kb][r], a.scale_log2, -lse2));
+                            const float p = !MASKED || r <= lim ? e : 0.f;
+                            d8[u] = p * (dp[kb][r] - dlt);
+                        }
+                        dsb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
                     }
-                    dsb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
                 }
-            }
+            };
+            if (full) scores_to_ds(std::false_type{});
+            else scores_to_ds(std::true_type{});
             // dQ^T += K^T dS^T
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int f = 0; f < 4 * C::DB; ++f) {
                 const int db = f % C::DB, j = (f / C::DB) % 2, kb = f / (2 * C::DB);
@@ -345,6 +367,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_s_setprio(0);
         }
         wait_vmem<0>();
         __syncthreads();
@@ -488,6 +511,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                 dp[r] = 0.f;
             }
             const lds_char* vst = (const lds_char*)smem;
+            __builtin_amdgcn_s_setprio(1);   // products first on a shared SIMD
 #pragma unroll
             for (int st = 0; st < C::DSTEPS; ++st) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -506,17 +530,21 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_s_setprio(0);
             // allowed: key present and (causal) at or before the row's
-            // position; dlo = position of row 16hh minus this lane's key
-            // (the tile's part is scalar, clamped to 32 bits)
+            // position: r + dlo >= 0, dlo = position of row 16hh minus this
+            // lane's key (the tile's part is scalar, clamped to 32 bits), or
+            // +-2^30 for every / no row
             const long long t64 = a.q_off + r0 - wg_first_kpos;
             const int tq = t64 > (1 << 30) ? (1 << 30) : (t64 < -(1 << 30) ? -(1 << 30) : (int)t64);
-            const int dlo = tq + lane_rel;
+            int dlo = a.causal ? tq + lane_rel : (1 << 30);
+            if (!key_ok) dlo = -(1 << 30);
             u32x4 pb[2], dsb[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                // lse (log2 units; a row without keys gets p = 0) and delta
-                // of rows 16hh + 8j .. +7 (the same for every lane of a half)
+                // lse (to log2 units) and delta of rows 16hh + 8j .. +7 (the
+                // same for every lane of a half). A row whose lse is -inf has
+                // no visible key, so the mask drops it after the exponential.
                 const int ro = 4 * (16 * hh + 8 * j);
                 const f32x4 l0 = *(const lds_f32x4*)(qt + 2 * TB + ro);
                 const f32x4 l1 = *(const lds_f32x4*)(qt + 2 * TB + ro + 16);
@@ -528,9 +556,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                     const int r = 8 * j + u;
                     const float l = u < 4 ? l0[u] : l1[u - 4];
                     const float dr = u < 4 ? d0[u] : d1[u - 4];
-                    const float l2 = l == -INFINITY ? INFINITY : l * kLog2e;
-                    const bool ok = key_ok && (!a.causal || r + dlo >= 0);
-                    const float p = ok ? fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l2)) : 0.f;
+                    const float e = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l * kLog2e));
+                    const float p = r + dlo >= 0 ? e : 0.f;
                     p8[u] = p;
                     d8[u] = p * (dp[r] - dr);
                 }
@@ -538,6 +565,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                 dsb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));
             }
             // dV^T += dO^T P, dK^T += Q^T dS
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int f = 0; f < 2 * C::DB; ++f) {
                 const int db = f % C::DB, j = f / C::DB;
@@ -554,6 +582,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_s_setprio(0);
         }
         wait_vmem<0>();
         __syncthreads();
