@@ -91,3 +91,23 @@ def test_backward_bidirectional_unequal_blocks_d64_gqa():
     for (o, l), gk, gv in zip(blocks, dk, dv):
         _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
         _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
+
+
+def test_backward_many_tiles_causal_gqa():
+    """A larger causal share: 1,100 query rows (34 row tiles and a ragged 12)
+    at positions 1100..2199 against a diagonal block and two unequal full
+    blocks (ragged against the 64-key and 128-key tiles), 16 query heads on
+    4 key/value heads, so that many workgroups of both gradient kernels are
+    resident together and every tile boundary case occurs."""
+    q, k, v, dout = _seq(1, 16, 4, 2200, 128, 4003)
+    q_off, Tq = 1100, 1100
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    ds = np.ascontiguousarray(dout[:, q_off:q_off + Tq])
+    blocks = [(1100, 1100), (0, 700), (700, 400)]
+    say(f"backward many tiles: blocks={blocks}")
+    dq, dk, dv = _run(qs, k, v, ds, blocks, q_off, True)
+    rq, rk, rv = oracle.attention_backward(qs, k, v, ds, q_off=q_off, k_off=0, causal=True)
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
