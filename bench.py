@@ -106,6 +106,94 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
 
 
+def bench_per_block(args):
+    """One rank's share through the per-block ring-step calls, as a ring over
+    several GPUs would drive them: cakv_state_init, then cakv_block_update for
+    each block in ring order r, r-1, ... (the running m, l, o in HBM between
+    calls; fully masked blocks launch nothing), then cakv_finalize. Same
+    useful FLOPs as the fused driver."""
+    import numpy as np
+    import torch
+
+    import cakv_synth as syn
+    import context_attention_kv_amd as cakv
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+    w = syn.WORKLOADS[args.config]
+    r = w.ranks[-1]
+    C = w.C
+    log(f"generating {w.name} (per-block calls)")
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    kd, vd = dev(syn.make_kv_full(w, "k")), dev(syn.make_kv_full(w, "v"))
+    qd = dev(syn.make_q_local(w, r))
+    blocks, _ = cakv.cakv_schedule(r, w.N, C, w.causal)
+    kb = {j: kd[:, j * C:(j + 1) * C].contiguous() for j in blocks}
+    vb = {j: vd[:, j * C:(j + 1) * C].contiguous() for j in blocks}
+    del kd, vd
+    m = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    o = torch.empty((w.B, C, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(o)
+    lse = torch.empty_like(m)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        cakv.cakv_state_init(m, l, o)
+        for j in blocks:
+            cakv.cakv_block_update(qd, kb[j], vb[j], r * C, j * C, w.causal, m, l, o)
+        cakv.cakv_finalize(m, l, o, out, lse)
+
+    for _ in range(max(args.warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    steps = max(args.steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = useful_flops(w, [r])
+    tf = flops / (ms * 1e-3) / 1e12
+    is_bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_F32_VALU_TFLOPS
+    rec = {
+        "metric": "per-block ring steps (state in HBM between calls): useful TFLOP/s",
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "N": w.N,
+                   "chunk": C, "d_k": w.D, "causal": w.causal, "ranks": [r],
+                   "calls": f"state_init + {len(blocks)} x block_update + finalize"},
+        "roofline": {"bound": "mfma" if is_bf16 else "alu",
+                     "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
+                     "achieved": round(tf, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "frac": round(tf / peak, 4), "traffic": None,
+                     "avg_call_ms": round(ms, 4), "flops_per_call": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_backward(args):
     """Gradients of one rank's share (dq, dk, dv from out, lse and a seeded
     upstream gradient): useful FLOPs = 2.5 x the forward's (five products of
@@ -278,6 +366,9 @@ def main():
     ap.add_argument("--no-aux", action="store_true", help="skip finalize/merge timing")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained matrix-core rate measurement")
+    ap.add_argument("--per-block", action="store_true",
+                    help="time the per-block ring-step calls (state_init, block_update per "
+                         "block, finalize) on --config's workload")
     ap.add_argument("--backward", action="store_true",
                     help="time cakv_backward_blocks on the 131,072-token causal context "
                          "(the million-token workload's shape at 1/8 length) instead")
@@ -296,6 +387,9 @@ def main():
         return
     if args.backward:
         bench_backward(args)
+        return
+    if args.per_block:
+        bench_per_block(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
