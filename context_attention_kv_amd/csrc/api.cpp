@@ -51,6 +51,8 @@ cakv_class classify(int64_t q_off, int64_t q_len, int64_t kv_off, int64_t kv_len
     return CAKV_DIAG;
 }
 
+constexpr long long kMaxHeadsTimesD = 1LL << 24;
+
 cakv_status check_common(int dtype, int B, int Hq, int Hkv, int Tq, int Tkv, int D) {
     if (dtype != CAKV_F32 && dtype != CAKV_BF16)
         return fail(CAKV_ERR_DTYPE, "dtype %d is neither CAKV_F32 nor CAKV_BF16", dtype);
@@ -60,6 +62,9 @@ cakv_status check_common(int dtype, int B, int Hq, int Hkv, int Tq, int Tkv, int
         return fail(CAKV_ERR_SHAPE, "heads must be positive with Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
                     Hq, Hkv);
     if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    // the kernels' per-tile buffer ranges (up to 64 rows of Hq * D bf16) are 32-bit
+    if ((long long)Hq * D > kMaxHeadsTimesD)
+        return fail(CAKV_ERR_SHAPE, "Hq * D = %lld above %lld", (long long)Hq * D, kMaxHeadsTimesD);
     return CAKV_OK;
 }
 
@@ -108,6 +113,8 @@ cakv_status decode_plan(int B, int Hq, int Hkv, int Tn, int D, const int64_t* kv
         return fail(CAKV_ERR_SHAPE, "heads must be positive with Hq %% Hkv == 0 (Hq=%d Hkv=%d)",
                     Hq, Hkv);
     if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
+    if ((long long)Hq * D > kMaxHeadsTimesD)
+        return fail(CAKV_ERR_SHAPE, "Hq * D = %lld above %lld", (long long)Hq * D, kMaxHeadsTimesD);
     if (n_portions < 1 || n_portions > CAKV_MAX_CHUNKS)
         return fail(CAKV_ERR_RANGE, "n_portions=%d outside [1, %d]", n_portions, CAKV_MAX_CHUNKS);
     if (!kv_len) return fail(CAKV_ERR_NULL, "kv_len_host is NULL");

@@ -44,7 +44,8 @@
  *     inputs are computed in fp32 throughout. State, lse and merge operands
  *     are always fp32.
  *   - scale <= 0 selects 1/sqrt(D).
- *   - Supported: D in {64, 128}; Hq % Hkv == 0; 16-byte aligned pointers;
+ *   - Supported: D in {64, 128}; Hq % Hkv == 0; Hq * D <= 2^24 (the
+ *     kernels address a tile's rows in 32 bits); 16-byte aligned pointers;
  *     sizes >= 0 (an empty problem returns CAKV_OK and launches nothing).
  *   - Errors: arguments are checked before anything is enqueued; on an error
  *     nothing is launched, outputs are untouched, the status is returned and

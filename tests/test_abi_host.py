@@ -123,6 +123,7 @@ def _bu(**kw):
     (dict(Hq=3, Hkv=2), 2), (dict(Hkv=0), 2), (dict(D=96), 2), (dict(q=NULL), 1),
     (dict(m=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1), (dict(q=MIS), 4),
     (dict(o=MIS), 4), (dict(k=MIS), 4), (dict(tc=FAKE + 4), 4),
+    (dict(Hq=1 << 18, Hkv=2), 2),
 ])
 def test_block_update_errors(kw, code):
     assert _bu(**kw) == code
@@ -210,6 +211,7 @@ def test_decode_errors_and_workspace_size():
     assert nb.value == 0
     assert L.cakv_decode_workspace_size(1, 8, 3, 4, 128, lens, 3, ctypes.byref(nb)) == 2
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 96, lens, 3, ctypes.byref(nb)) == 2
+    assert L.cakv_decode_workspace_size(1, 1 << 18, 2, 4, 128, lens, 3, ctypes.byref(nb)) == 2
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, lens, 0, ctypes.byref(nb)) == 5
     assert L.cakv_decode_workspace_size(1, 8, 2, 4, 128, None, 3, ctypes.byref(nb)) == 1
     bad = (I64 * 1)(-1)
