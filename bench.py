@@ -232,7 +232,8 @@ def bench_backward(args):
     dq = torch.empty_like(out)
     dk = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in kb]
     dv = [torch.empty(t.shape, dtype=torch.float32, device="cuda") for t in kb]
-    ws = torch.empty(w.B * w.Hq * C, dtype=torch.float32, device="cuda")
+    ws = torch.empty(cakv.cakv_backward_workspace_size(w.B, w.Hq, C) // 4, dtype=torch.float32,
+                     device="cuda")
     stream = torch.cuda.current_stream()
 
     def call():

@@ -295,6 +295,14 @@ def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: S
                                     _stream(stream)), "cakv_forward_blocks")
 
 
+def cakv_backward_workspace_size(B: int, Hq: int, Tq: int) -> int:
+    """Bytes of workspace cakv_backward_blocks needs for these sizes."""
+    out = ctypes.c_int64()
+    _check(_lib.cakv_backward_workspace_size(B, Hq, Tq, ctypes.byref(out)),
+           "cakv_backward_workspace_size")
+    return int(out.value)
+
+
 def cakv_backward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: Sequence[int],
                          q_offset: int, causal: bool, out, lse, dout, dq, dk_blocks: Sequence,
                          dv_blocks: Sequence, workspace=None, scale: float = 0.0, stream=None):
@@ -314,7 +322,8 @@ def cakv_backward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: 
             raise ValueError("blocks and their gradients must all be [B, L_t, Hkv, D]")
     if workspace is None:
         import torch
-        workspace = torch.empty(max(B * Hq * Tq, 4), dtype=torch.float32, device=q.device)
+        nbytes = cakv_backward_workspace_size(B, Hq, Tq)
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
 
     def arr(ts):

@@ -381,7 +381,7 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
 cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host) {
     if (!bytes_host) return fail(CAKV_ERR_NULL, "bytes_host is NULL");
     if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
-    *bytes_host = (int64_t)B * Hq * Tq * 4;
+    *bytes_host = (int64_t)B * Hq * Tq * 8;   // delta, then lse in log2 units
     return ok();
 }
 
@@ -412,9 +412,9 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
     if (Tq > 0 && (!q || !out || !lse || !dout || !dq))
         return fail(CAKV_ERR_NULL, "q, out, lse, dout or dq is NULL");
     if (Tq > 0 && !workspace) return fail(CAKV_ERR_NULL, "workspace is NULL");
-    if (workspace_bytes < (int64_t)B * Hq * Tq * 4)
+    if (workspace_bytes < (int64_t)B * Hq * Tq * 8)
         return fail(CAKV_ERR_SHAPE, "workspace of %lld bytes, %lld needed",
-                    (long long)workspace_bytes, (long long)B * Hq * Tq * 4);
+                    (long long)workspace_bytes, (long long)B * Hq * Tq * 8);
     if ((Tq > 0 && (!aligned16(q) || !aligned16(out) || !aligned16(dout) || !aligned16(dq))) ||
         !aligned16(workspace))
         return fail(CAKV_ERR_ALIGN, "q/out/dout/dq/workspace not 16-byte aligned");
@@ -453,6 +453,7 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
     a.scale_log2 = a.scale * 1.4426950408889634f;
     a.causal = causal ? 1 : 0;
     a.delta = static_cast<float*>(workspace);
+    a.lse2 = a.delta + (long long)B * Hq * Tq;
     a.dq = dq;
     const int G = Hq / Hkv;
     const long long npblk = (Tq + 31) / 32;

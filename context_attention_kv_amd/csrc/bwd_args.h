@@ -31,6 +31,7 @@ struct BwdArgs {
     float scale_log2;                       // scale * log2(e)
     int causal;
     float* delta;                           // [B, Hq, Tq] workspace: rowsum(dout * out)
+    float* lse2;                            // [B, Hq, Tq] workspace: lse * log2(e), +inf for -inf
     float* dq;                              // [B, Tq, Hq, D] fp32
     int wg_per_bg;                          // dq kernel: workgroups per (batch, kv head)
 };

@@ -165,6 +165,8 @@ __device__ __forceinline__ unsigned region_off(int lr, int lane, long long rs) {
 }
 
 // ---------------------------------------------------------------- delta
+// delta and the row's lse in log2 units (+inf for a row without keys, so that
+// every p of that row is 0), per query row
 template <int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
     constexpr int PER = D / 64;
@@ -181,7 +183,10 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
     if (lane == 0) {
         const long long h = row % a.Hq, bi = row / a.Hq;
         const long long i = bi % a.Tq, b = bi / a.Tq;
-        a.delta[(b * a.Hq + h) * a.Tq + i] = s;
+        const long long si = (b * a.Hq + h) * a.Tq + i;
+        a.delta[si] = s;
+        const float l = a.lse[si];
+        a.lse2[si] = l == -INFINITY ? INFINITY : l * kLog2e;
     }
 }
 
@@ -485,7 +490,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
         }
         if (wave < 2) {
             const long long si = ((long long)b * a.Hq + h) * a.Tq + r0;
-            const i32x4 rs = make_rsrc(wave == 0 ? a.lse + si : a.delta + si, (unsigned)(rows * 4));
+            const i32x4 rs = make_rsrc(wave == 0 ? a.lse2 + si : a.delta + si, (unsigned)(rows * 4));
             copy4_to_lds(rs, (unsigned)(4 * lane), dst + 2 * TB + 256 * wave);
         }
     };
@@ -542,9 +547,8 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
             u32x4 pb[2], dsb[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                // lse (to log2 units) and delta of rows 16hh + 8j .. +7 (the
-                // same for every lane of a half). A row whose lse is -inf has
-                // no visible key, so the mask drops it after the exponential.
+                // lse (log2 units) and delta of rows 16hh + 8j .. +7 (the same
+                // for every lane of a half)
                 const int ro = 4 * (16 * hh + 8 * j);
                 const f32x4 l0 = *(const lds_f32x4*)(qt + 2 * TB + ro);
                 const f32x4 l1 = *(const lds_f32x4*)(qt + 2 * TB + ro + 16);
@@ -556,7 +560,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
                     const int r = 8 * j + u;
                     const float l = u < 4 ? l0[u] : l1[u - 4];
                     const float dr = u < 4 ? d0[u] : d1[u - 4];
-                    const float e = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l * kLog2e));
+                    const float e = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l));
                     const float p = r + dlo >= 0 ? e : 0.f;
                     p8[u] = p;
                     d8[u] = p * (dp[r] - dr);

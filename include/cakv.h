@@ -239,8 +239,9 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
  * dq: [B, Tq, Hq, D] fp32; dk_blocks_host, dv_blocks_host: HOST arrays of
  *   device pointers, block t = [B, kv_len_host[t], Hkv, D] fp32. All outputs
  *   are overwritten (a block no query sees gets zeros).
- * workspace: device buffer of cakv_backward_workspace_size bytes (the
- *   per-row delta), 16-byte aligned, owned by the caller.
+ * workspace: device buffer of cakv_backward_workspace_size bytes (per
+ *   row: delta = dout . out and the lse in log2 units), 16-byte aligned,
+ *   owned by the caller.
  * Errors: CAKV_ERR_DTYPE unless dtype = CAKV_BF16; otherwise as for
  * cakv_forward_blocks, plus NULL out / lse / dout / dq / gradient block
  * pointers and a too small workspace (CAKV_ERR_SHAPE).
@@ -254,7 +255,7 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
                                  float* const* dv_blocks_host, void* workspace,
                                  int64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace cakv_backward_blocks needs (B * Hq * Tq * 4), written
+/* Bytes of workspace cakv_backward_blocks needs (B * Hq * Tq * 8), written
  * to the HOST int64 *bytes_host. */
 cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host);
 

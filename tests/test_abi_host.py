@@ -263,10 +263,10 @@ def test_backward_errors():
     offs = (I64 * 1)(0)
     ptrs = (ctypes.c_void_p * 1)(FAKE)
     nb = I64(0)
-    assert L.cakv_backward_workspace_size(2, 8, 300, ctypes.byref(nb)) == 0 and nb.value == 2 * 8 * 300 * 4
+    assert L.cakv_backward_workspace_size(2, 8, 300, ctypes.byref(nb)) == 0 and nb.value == 2 * 8 * 300 * 8
     assert L.cakv_backward_workspace_size(-1, 8, 300, ctypes.byref(nb)) == 2
 
-    def bw(dtype=1, n=1, D=128, q=FAKE, dout=FAKE, ws=FAKE, wsb=8 * 50 * 4, dk=ptrs):
+    def bw(dtype=1, n=1, D=128, q=FAKE, dout=FAKE, ws=FAKE, wsb=8 * 50 * 8, dk=ptrs):
         return L.cakv_backward_blocks(q, ptrs, ptrs, lens, offs, n, dtype, 1, 8, 2, 50, D, 100, 1,
                                       0.0, FAKE, FAKE, dout, FAKE, dk, ptrs, ws, wsb, None)
     assert bw(dtype=0) == 3
