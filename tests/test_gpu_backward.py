@@ -6,12 +6,16 @@ gradient dout; the oracle differentiates the plain definition in fp64 on the
 same stored values.
 
 Tolerance, per gradient tensor, relative to the reference's scale
-(rms = root-mean-square of the reference tensor): max |d| <= 5e-2 * rms' and
+(rms = root-mean-square of the reference tensor): max |d| <= 1e-1 * rms' and
 mean |d| <= 4e-3 * rms', rms' = max(rms, 1e-3). The kernels round p and ds to
 bf16 (relative error up to 2^-9 ~ 2e-3, rms ~1.1e-3) before the products that
 sum them over keys or rows, so a gradient entry's error is ~1e-3 of the rms of
 its terms (measured: mean |d| ~1.3e-3 rms); the largest of ~10^5 entries
-lands about 20 times higher (measured up to 2.3e-2 rms), hence the max bound.
+lands about 20 times higher (up to 2.3e-2 rms on rows that see many keys).
+A row that sees only two keys carries a gradient several times the tensor's
+rms, and there the rounding of ds alone gives 6.0e-2 rms (an fp64 model of
+dq with only ds rounded to bf16 reproduces the kernel's largest error on
+test_backward_rows_without_keys to four digits), hence the max bound.
 """
 import numpy as np
 import pytest
@@ -42,7 +46,7 @@ def _check(name, got, ref):
     st = dict(max=float(d.max()), mean=float(d.mean()), rms_ref=rms)
     say(f"  {name}: {st}")
     assert not np.isnan(got).any(), name
-    assert st["max"] <= 5e-2 * rms, (name, st)
+    assert st["max"] <= 1e-1 * rms, (name, st)
     assert st["mean"] <= 4e-3 * rms, (name, st)
 
 
@@ -111,3 +115,26 @@ def test_backward_many_tiles_causal_gqa():
     for (o, l), gk, gv in zip(blocks, dk, dv):
         _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
         _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
+
+
+def test_backward_rows_without_keys():
+    """Causal rows 0..99 precede every key (blocks start at position 100):
+    their lse is -inf, their out 0, and they give no gradient anywhere; the
+    rest of the rows see a diagonal block, and a block lies wholly after all
+    of them."""
+    q, k, v, dout = _seq(1, 8, 2, 500, 128, 4004)
+    Tq = 300
+    qs = np.ascontiguousarray(q[:, :Tq])
+    ds = np.ascontiguousarray(dout[:, :Tq])
+    blocks = [(100, 300), (400, 100)]
+    dq, dk, dv = _run(qs, k, v, ds, blocks, 0, True)
+    # the oracle sees exactly the blocks' keys: positions 100..499
+    ks = np.ascontiguousarray(k[:, 100:])
+    vs = np.ascontiguousarray(v[:, 100:])
+    rq, rk, rv = oracle.attention_backward(qs, ks, vs, ds, q_off=0, k_off=100, causal=True)
+    assert not dq[:, :100].any(), "rows without keys must get no gradient"
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, o - 100:o - 100 + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, o - 100:o - 100 + l])
+    assert not dk[1].any() and not dv[1].any()
