@@ -72,20 +72,26 @@ float resolve_scale(float scale, int D) {
     return scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
 }
 
-// Fill the workgroup geometry of a forward launch.
-void set_grid(cakv::FwdArgs& a, int dtype, int D) {
+// Fill the workgroup geometry of a forward launch (the grid is at most
+// 2^31 - 1 workgroups).
+cakv_status set_grid(cakv::FwdArgs& a, int dtype, int D) {
     (void)D;
+    long long per_bg, n_wg;
     if (dtype == CAKV_BF16) {
-        const int nw = cakv::fwd_bf16_waves();
-        const int G = a.Hq / a.Hkv;
-        const long long npblk = (a.Tq + 31) / 32;   // 32 query rows per wave
-        a.wg_per_bg = (int)((G * npblk + nw - 1) / nw);
-        a.n_wg = (int)((long long)a.B * a.Hkv * a.wg_per_bg);
+        const long long nw = cakv::fwd_bf16_waves();
+        const long long G = a.Hq / a.Hkv;
+        const long long npblk = (a.Tq + 31LL) / 32;   // 32 query rows per wave
+        per_bg = (G * npblk + nw - 1) / nw;
+        n_wg = (long long)a.B * a.Hkv * per_bg;
     } else {
-        const int rows = cakv::fwd_f32_wg_rows();
-        a.wg_per_bg = (a.Tq + rows - 1) / rows;
-        a.n_wg = (int)((long long)a.B * a.Hq * a.wg_per_bg);
+        const long long rows = cakv::fwd_f32_wg_rows();
+        per_bg = (a.Tq + rows - 1) / rows;
+        n_wg = (long long)a.B * a.Hq * per_bg;
     }
+    if (n_wg > 2147483647LL) return fail(CAKV_ERR_SHAPE, "forward grid too large (%lld workgroups)", n_wg);
+    a.wg_per_bg = (int)per_bg;
+    a.n_wg = (int)n_wg;
+    return CAKV_OK;
 }
 
 int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
@@ -231,7 +237,8 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
     a.load_state = 1;
     a.store_state = 1;
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
-    set_grid(a, dtype, D);
+    s = set_grid(a, dtype, D);
+    if (s != CAKV_OK) return s;
     return hip_status(launch_fwd(a, dtype, D, stream), "block_update launch");
 }
 
@@ -320,7 +327,8 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     a.out_bf16 = out_dtype == CAKV_BF16;
     a.lse = lse;
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
-    set_grid(a, dtype, D);
+    s = set_grid(a, dtype, D);
+    if (s != CAKV_OK) return s;
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
 }
 
@@ -374,7 +382,8 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     a.out_bf16 = out_dtype == CAKV_BF16;
     a.lse = lse;
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
-    set_grid(a, dtype, D);
+    s = set_grid(a, dtype, D);
+    if (s != CAKV_OK) return s;
     return hip_status(launch_fwd(a, dtype, D, stream), "forward_blocks launch");
 }
 
@@ -457,7 +466,10 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
     a.dq = dq;
     const int G = Hq / Hkv;
     const long long npblk = (Tq + 31) / 32;
-    a.wg_per_bg = (int)((G * npblk + 3) / 4);
+    const long long dq_per_bg = (G * npblk + 3) / 4;
+    if ((long long)B * Hkv * dq_per_bg > 2147483647LL)
+        return fail(CAKV_ERR_SHAPE, "backward grid too large");
+    a.wg_per_bg = (int)dq_per_bg;
     if (Tq == 0) {
         // no queries: every key gradient is zero (the dK/dV kernel visits no query tile)
         a.wg_per_bg = 0;

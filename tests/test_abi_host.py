@@ -124,6 +124,7 @@ def _bu(**kw):
     (dict(m=NULL), 1), (dict(k=NULL), 1), (dict(v=NULL), 1), (dict(q=MIS), 4),
     (dict(o=MIS), 4), (dict(k=MIS), 4), (dict(tc=FAKE + 4), 4),
     (dict(Hq=1 << 18, Hkv=2), 2),
+    (dict(B=1 << 16, Hq=1 << 10, Hkv=1 << 10, Tq=1 << 20), 2),   # grid above 2^31 - 1
 ])
 def test_block_update_errors(kw, code):
     assert _bu(**kw) == code
