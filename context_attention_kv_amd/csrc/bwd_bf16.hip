@@ -164,6 +164,15 @@ __device__ __forceinline__ unsigned region_off(int lr, int lane, long long rs) {
     return (unsigned)(2 * (row * rs + 8 * (p ^ swz<D>(row))));
 }
 
+// Workgroup id -> logical id. Ids are dealt to the 8 XCDs round robin; this
+// gives each XCD a contiguous range of logical ids, so the workgroups that
+// stream the same key/value (or query) head run on one XCD and share its L2.
+__device__ __forceinline__ int xcd_logical(int bid, int n) {
+    const int per = n / 8, rem = n % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
 // ---------------------------------------------------------------- delta
 // delta and the row's lse in log2 units (+inf for a row without keys, so that
 // every p of that row is 0), per query row
@@ -202,7 +211,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
 
-    const int bg = blockIdx.x / a.wg_per_bg, qt = blockIdx.x % a.wg_per_bg;
+    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int bg = logical / a.wg_per_bg;
+    const int qt = a.wg_per_bg - 1 - logical % a.wg_per_bg;   // heaviest (latest rows) first
     const int b = bg / a.Hkv, g = bg % a.Hkv, G = a.Hq / a.Hkv;
     const int npblk = (a.Tq + 31) / 32;
     const int task = qt * 4 + wave, pblk = task / G, h = g * G + task % G;
@@ -410,7 +421,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     const int l32 = lane & 31, hh = lane >> 5;
 
     const int ntiles = a.kt0[a.n_blocks];
-    int id = blockIdx.x;
+    int id = xcd_logical(blockIdx.x, gridDim.x);   // key tiles of one head in order on one XCD
     const int kt = id % ntiles;
     id /= ntiles;
     const int g = id % a.Hkv, b = id / a.Hkv, G = a.Hq / a.Hkv;
