@@ -486,8 +486,15 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     unsigned cp_off[NCP];
 #pragma unroll
     for (int n = 0; n < NCP; ++n) cp_off[n] = region_off<D>(4 * n + wave, lane, q_rs);
-    auto issue = [&](int n, unsigned dst) {
-        const int hj = n % G, rt = rt0 + n / G;
+    // query tiles go head-fastest: tile n is head n % G of row block
+    // rt0 + n / G; running counters instead of divisions
+    int i_hj = 0, i_rt = rt0;   // the next tile to copy
+    auto issue = [&](unsigned dst) {
+        const int hj = i_hj, rt = i_rt;
+        if (++i_hj == G) {
+            i_hj = 0;
+            ++i_rt;
+        }
         const int h = g * G + hj;
         const int r0 = rt * QR, rows = min(QR, a.Tq - r0);
         const long long base = ((long long)b * a.Tq + r0) * q_rs + (long long)h * D;
@@ -507,17 +514,24 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     };
     // the K and V loads above, in a form the compiler's wait tracking sees
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (nq > 0) issue(0, lds0 + VT);
+    if (nq > 0) issue(lds0 + VT);
+    // the tile being computed: head c_hj of its group; c_tq = position of its
+    // first row minus the workgroup's first key, saturated at 2^30 (with the
+    // causal rule the first visited tile has c_tq >= -31, and it only grows)
+    int c_hj = 0, c_tq;
+    {
+        const long long rel0 = a.q_off + (long long)rt0 * QR - wg_first_kpos;
+        c_tq = rel0 > (1 << 30) ? (1 << 30) : (rel0 < -(1 << 30) ? -(1 << 30) : (int)rel0);
+    }
     wait_vmem<0>();
     __syncthreads();
     for (int n = 0; n < nq; ++n) {
         const int buf = n & 1;
         // the other buffer was last read before the barrier that ended the
         // previous step
-        if (n + 1 < nq) issue(n + 1, lds0 + VT + (buf ^ 1) * BUF);
+        if (n + 1 < nq) issue(lds0 + VT + (buf ^ 1) * BUF);
         const lds_char* qt = (const lds_char*)smem + VT + buf * BUF;
         const lds_char* dt = qt + TB;
-        const int r0 = (rt0 + n / G) * QR;
         {
             // S = Q K^T, dP = dO V^T: s[r] = score(row r0 + 16hh + r, key)
             f32x16 s, dp;
@@ -551,9 +565,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
             // position: r + dlo >= 0, dlo = position of row 16hh minus this
             // lane's key (the tile's part is scalar, clamped to 32 bits), or
             // +-2^30 for every / no row
-            const long long t64 = a.q_off + r0 - wg_first_kpos;
-            const int tq = t64 > (1 << 30) ? (1 << 30) : (t64 < -(1 << 30) ? -(1 << 30) : (int)t64);
-            int dlo = a.causal ? tq + lane_rel : (1 << 30);
+            int dlo = a.causal ? c_tq + lane_rel : (1 << 30);
             if (!key_ok) dlo = -(1 << 30);
             u32x4 pb[2], dsb[2];
 #pragma unroll
@@ -598,6 +610,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_s_setprio(0);
+        }
+        if (++c_hj == G) {   // next row block: its first row is QR positions later
+            c_hj = 0;
+            c_tq = min(c_tq, (1 << 30) - QR) + QR;
         }
         wait_vmem<0>();
         __syncthreads();
