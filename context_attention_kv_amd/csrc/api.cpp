@@ -75,11 +75,10 @@ float resolve_scale(float scale, int D) {
 // Fill the workgroup geometry of a forward launch (the grid is at most
 // 2^31 - 1 workgroups).
 cakv_status set_grid(cakv::FwdArgs& a, int dtype, int D) {
-    (void)D;
     long long per_bg, n_wg;
     if (dtype == CAKV_BF16) {
-        const long long nw = cakv::fwd_bf16_waves();
         const long long G = a.Hq / a.Hkv;
+        const long long nw = cakv::fwd_bf16_waves(D, (int)G);
         const long long npblk = (a.Tq + 31LL) / 32;   // 32 query rows per wave
         per_bg = (G * npblk + nw - 1) / nw;
         n_wg = (long long)a.B * a.Hkv * per_bg;

@@ -34,6 +34,11 @@
 //   * workgroup ids are remapped so that each XCD works through a contiguous
 //     range of (batch, kv head) pairs (their K/V stream then hits that XCD's
 //     L2), heaviest query tiles first.
+// That ping-pong kernel serves grouped-query shares at d = 128. Every other
+// shape (d = 64; d = 128 with one query head per kv head) goes to a four-wave
+// kernel with the same tile arithmetic: one wave per SIMD, several
+// workgroups per CU running free of each other, a double buffer of tiles and
+// one barrier per tile (fwd_bf16_4w_kernel below).
 #include <hip/hip_runtime.h>
 
 #include "fwd_args.h"
@@ -603,20 +608,343 @@ fwd_bf16_kernel(const FwdArgs a) {
     }
 }
 
+// Four-wave variant: one wave per SIMD, several workgroups per CU running
+// free of each other (no phase lock): each tile is copied into a double
+// buffer, then every wave runs Q K^T, the softmax and P V on it at raised
+// priority for the products, and one barrier ends the step. It keeps more
+// independent waves per CU at d = 64 (four workgroups) and fills small grids;
+// the ping-pong kernel above serves grouped-query shares at d = 128, whose
+// long K/V streams favour its larger workgroups.
+template <int D, bool COUNT>
+__global__ void __launch_bounds__(256, 2)
+fwd_bf16_4w_kernel(const FwdArgs a) {
+    using C = Cfg<D>;
+    constexpr int NW = 4;
+    constexpr int RW = 32;
+    // double buffer: [K tile | V tile], each [64 keys][D] bf16, swizzled
+    __shared__ __attribute__((aligned(1024))) char smem[2 * C::BUF_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int l32 = lane & 31, hh = lane >> 5;
+    const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;   // LDS address of the buffers
+
+    // ---- workgroup -> (batch, kv head, query tile); XCD-contiguous order ----
+    const int bid = blockIdx.x;
+    const int per = a.n_wg / 8, rem = a.n_wg % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    const int bg = logical / a.wg_per_bg;
+    const int qt = a.wg_per_bg - 1 - (logical % a.wg_per_bg);  // heaviest first
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int G = a.Hq / a.Hkv;
+    const int npblk = (a.Tq + RW - 1) / RW;
+
+    const int task = qt * NW + wave;
+    const int pblk = task / G;
+    const int h = g * G + task % G;
+    const bool wave_valid = pblk < npblk;
+    const int row0 = pblk * RW;
+    int last_pblk = (qt * NW + NW - 1) / G;
+    if (last_pblk > npblk - 1) last_pblk = npblk - 1;
+    const int wg_last_row = min(a.Tq, (last_pblk + 1) * RW) - 1;
+    const long long wg_last_pos = a.q_off + wg_last_row;
+    const int wave_rows = wave_valid ? min(RW, a.Tq - row0) : 0;
+    const long long wave_first_pos = a.q_off + row0;
+
+    const long long q_rs = (long long)a.Hq * D;
+    const long long kv_rs = (long long)a.Hkv * D;
+
+    // ---- Q^T fragments (B operand): lane (l32, hh) holds Q[row][16s+8hh .. +7] ----
+    u32x4 qf[C::DSTEPS];
+    {
+        const int row = row0 + l32;
+        const bool ok = wave_valid && row < a.Tq;
+        const __bf16* qb = static_cast<const __bf16*>(a.q) +
+                           ((long long)b * a.Tq + (ok ? row : 0)) * q_rs + (long long)h * D;
+#pragma unroll
+        for (int s = 0; s < C::DSTEPS; ++s)
+            qf[s] = ok ? *reinterpret_cast<const u32x4*>(qb + 16 * s + 8 * hh)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    // ---- running state: lane owns query column l32 ----
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o_acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o_acc[db][r] = 0.f;
+    if (a.load_state && wave_valid) {
+        const float log2e = 1.44269504088896341f;
+        const int row = row0 + l32;
+        const bool ok = row < a.Tq;
+        const long long si = ((long long)b * a.Hq + h) * a.Tq + (ok ? row : 0);
+        const float mv = ok ? a.m[si] : -INFINITY;
+        const float lv = ok ? a.l[si] : 0.f;
+        m_run = mv * log2e;
+        l_run = hh == 0 ? lv : 0.f;
+        const float* orow = a.o + (((long long)b * a.Tq + (ok ? row : 0)) * a.Hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            f32x16 acc;
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const f32x4 x = ok ? *reinterpret_cast<const f32x4*>(orow + 32 * db + 8 * ib + 4 * hh)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[4 * ib + jj] = x[jj];
+            }
+            o_acc[db] = acc;
+        }
+    }
+
+    // ---- lane-constant LDS offsets of the operand reads ----
+    const int k_row = key_of_row(l32) * C::ROW_BYTES;
+    const int kx = kswz<D>(key_of_row(l32));
+    const int g16 = lane >> 4, src = lane & 15;
+    const int v_key = 16 * (g16 >> 1) + (src >> 2);
+    const int v_dim = 16 * (g16 & 1) + 4 * (src & 3);
+    const int v_sw = vswz<D>(src >> 2);
+
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the Q and state loads
+    unsigned n_full = 0, n_masked = 0;
+
+    // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
+    const HeadAt at{b, g, kv_rs, D, wg_last_pos, wave_first_pos, a.causal};
+    int T = 0;
+    for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
+
+    // Tile copies: copy n of every wave fills 1 KB region 4n + wave of the K
+    // and of the V tile.
+    constexpr int LOADS = C::REGIONS / 4;
+    unsigned cpk[LOADS], cpv[LOADS];
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+        const int row = (n * 4 + wave) * C::ROWS_PER_KB + lane / C::UNITS;
+        const int p = lane % C::UNITS;
+        cpk[n] = (unsigned)(2 * (row * kv_rs + 8 * (p ^ kswz<D>(row))));
+        cpv[n] = (unsigned)(2 * (row * kv_rs + 8 * (p ^ vswz<D>(row))));
+    }
+    Cursor ld = cursor_first(a, at);   // next tile to copy
+    auto issue = [&](unsigned buf) {
+        const int key0 = ld.ti * kBK;
+        const int rows = min(kBK, ld.len - key0);
+        const unsigned bytes = (unsigned)(rows * kv_rs * 2);
+        const i32x4 rk = make_rsrc(ld.kp + (long long)key0 * kv_rs, bytes);
+        const i32x4 rv = make_rsrc(ld.vp + (long long)key0 * kv_rs, bytes);
+#pragma unroll
+        for (int n = 0; n < LOADS; ++n) {
+            copy16_to_lds(rk, cpk[n], buf + (n * 4 + wave) * 1024);
+            copy16_to_lds(rv, cpv[n], buf + C::TILE_BYTES + (n * 4 + wave) * 1024);
+        }
+        cursor_next(a, at, ld);
+    };
+    if (T > 0) issue(lds0);
+    wait_vmem<0>();
+    __syncthreads();
+
+    auto v_frag = [&](const lds_char* vt, int i) -> u32x4 {
+        const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
+        const int key = 32 * kb + 8 * j + v_key;
+        const int d = 32 * db + v_dim;
+        const int off = key * C::ROW_BYTES + 16 * ((d >> 3) ^ v_sw) + 2 * (d & 7);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vt + off + 4 * C::ROW_BYTES));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+        return u32x4{l2[0], l2[1], h2[0], h2[1]};
+    };
+    auto k_frag = [&](const lds_char* kt, int i) -> u32x4 {
+        const int st = i / 2, kb = i % 2;
+        return *(const lds_u32x4*)(kt + kb * 32 * C::ROW_BYTES + k_row + 16 * ((2 * st + hh) ^ kx));
+    };
+    constexpr int NPV = 4 * C::DB;       // P V products per tile
+    constexpr int NQK = 2 * C::DSTEPS;   // Q K^T products per tile
+
+    Cursor cq = cursor_first(a, at);   // tile this wave computes
+    for (int t = 0; t < T; ++t) {
+        const int buf = t & 1;
+        // the other buffer was last read before the barrier that ended the
+        // previous step
+        if (t + 1 < T) issue(lds0 + (buf ^ 1) * C::BUF_BYTES);
+        const lds_char* kt = (const lds_char*)(smem + buf * C::BUF_BYTES);
+        const lds_char* vt = kt + C::TILE_BYTES;
+        // tile t against this wave's rows: k0r = position of the tile's key 0
+        // minus the wave's first query position
+        const int key0 = cq.ti * kBK;
+        const int tile_keys = min(kBK, cq.len - key0);
+        const int k0r = cq.all_full ? -(1 << 30) : min(cq.rel, kBK) + key0;
+        const bool full = k0r + tile_keys - 1 <= 0;
+        const bool cmp = wave_valid && k0r <= wave_rows - 1;
+        const bool need_mask = !full || tile_keys < kBK;
+        if constexpr (COUNT) {
+            n_full += cmp && full ? 1u : 0u;
+            n_masked += cmp && !full ? 1u : 0u;
+        }
+        if (cmp) {
+            // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
+            __builtin_amdgcn_s_setprio(1);   // products first on the shared SIMD
+            f32x16 s[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+            for (int i = 0; i < NQK; ++i)
+                s[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(k_frag(kt, i)), as_bf16x8(qf[i / 2]), s[i % 2], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NQK - 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_s_setprio(0);
+            if (need_mask) {
+                const int dq = l32 - k0r;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int run0 = 32 * kb + 16 * hh;
+                    int lim = tile_keys - 1 - run0;
+                    if (a.causal) lim = min(lim, dq - run0);
+                    const i32x16 ridx = {0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
+                    const f32x16 ninf = -INFINITY;
+                    s[kb] = ridx <= lim ? s[kb] : ninf;
+                }
+            }
+            // online softmax (log2 domain: t = score * scale * log2 e)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = half_max(mx);
+            const float m_new = fmaxf(m_run, mx * a.scale_log2);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) o_acc[db] *= alpha;
+            }
+            float rs = 0.f;
+            u32x4 pb[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    f32x8 p;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        p[u] = fast_exp2(__builtin_fmaf(s[kb][8 * j + u], a.scale_log2, -m_use));
+                        rs += p[u];
+                    }
+                    pb[kb][j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p, bf16x8));
+                }
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+            // O^T += V^T P^T
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+                const int db = i % C::DB, j = (i / C::DB) % 2, kb = i / (2 * C::DB);
+                o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(v_frag(vt, i)), as_bf16x8(pb[kb][j]), o_acc[db], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < NPV - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        cursor_next(a, at, cq);
+        // this wave's copies of tile t+1 must have landed before the barrier
+        // that publishes it
+        wait_vmem<0>();
+        __syncthreads();
+    }
+
+    // ---- epilogue: store state, or finalise into out / lse ----
+    if (wave_valid) {
+        const int row = row0 + l32;
+        const float l_tot = half_sum(l_run);
+        if (row < a.Tq) {
+            const long long si = ((long long)b * a.Hq + h) * a.Tq + row;
+            const long long oi = (((long long)b * a.Tq + row) * a.Hq + h) * D;
+            if (a.store_state) {
+                if (hh == 0) {
+                    a.m[si] = m_run * kLn2;
+                    a.l[si] = l_tot;
+                }
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        f32x4 x;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) x[jj] = o_acc[db][4 * ib + jj];
+                        *reinterpret_cast<f32x4*>(a.o + oi + 32 * db + 8 * ib + 4 * hh) = x;
+                    }
+            } else {
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                if (hh == 0 && a.lse)
+                    a.lse[si] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        f32x4 x;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) x[jj] = o_acc[db][4 * ib + jj] * inv;
+                        const int d = 32 * db + 8 * ib + 4 * hh;
+                        if (a.out_bf16) {
+                            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+                            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + oi + d) =
+                                __builtin_convertvector(x, bf16x4);
+                        } else {
+                            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi + d) = x;
+                        }
+                    }
+            }
+        }
+    }
+    if (COUNT && lane == 0 && (n_full | n_masked)) {
+        atomicAdd(a.counters + 0, (unsigned long long)n_full);
+        atomicAdd(a.counters + 1, (unsigned long long)n_masked);
+    }
+}
+
+// Which kernel serves a shape: the ping-pong kernel for grouped-query shares
+// at d = 128 (measured faster there: 1,039 against 910 TFLOP/s on the
+// million-token share), the four-wave kernel otherwise (d = 64 bidirectional
+// +43 %, small d = 128 shares +36 %, the B=8 H=64 T=32768 share +4 %).
+bool use_four_waves(int D, int G) { return D == 64 || G == 1; }
+
 template <int D>
 int launch(const FwdArgs& a, void* stream) {
-    if (a.counters)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
-                           static_cast<hipStream_t>(stream), a);
-    else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0,
-                           static_cast<hipStream_t>(stream), a);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (use_four_waves(D, a.Hq / a.Hkv)) {
+        if (a.counters)
+            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, true>), dim3(a.n_wg), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, false>), dim3(a.n_wg), dim3(256), 0, s, a);
+    } else if (a.counters) {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0, s, a);
+    }
     return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int fwd_bf16_waves() { return 8; }
+int fwd_bf16_waves(int D, int G) { return use_four_waves(D, G) ? 4 : Cfg<128>::NW; }
 
 int launch_fwd_bf16(const FwdArgs& a, int D, void* stream) {
     if (D == 128) return launch<128>(a, stream);
