@@ -186,10 +186,14 @@ def test_finalize_empty_rows():
     assert torch.all(out == 0) and torch.all(lse == -float("inf"))
 
 
-def test_poisoned_skipped_blocks_and_future_keys():
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 2, 128), (4, 4, 128), (4, 4, 64)])
+def test_poisoned_skipped_blocks_and_future_keys(Hq, Hkv, D):
     """NaN in blocks the causal schedule skips must never be read; huge finite
-    values at future positions inside the diagonal block must add exactly 0."""
-    w = syn.scaled(SMALL, B=1)
+    values at future positions inside the diagonal block must add exactly 0.
+    Grouped heads at d=128 run the ping-pong kernel, the other shapes the
+    four-wave kernel."""
+    w = syn.scaled(SMALL, B=1, Hq=Hq, Hkv=Hkv, D=D,
+                   k_head_mul=tuple(8.0 if g % 2 else 1.0 for g in range(Hkv)))
     inp = Inputs(w, ranks=(1,))
     out0, lse0, _ = run_forward(inp, 1)
     C = w.C
