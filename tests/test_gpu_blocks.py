@@ -58,11 +58,17 @@ def test_state_init_values():
     assert torch.all(m == -float("inf")) and torch.all(l == 0) and torch.all(o == 0)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_per_block_ring_equals_oracle_and_state(dtype):
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [
+    ("bf16", 4, 2, 128),   # grouped heads at d=128: the ping-pong kernel
+    ("f32", 4, 2, 128),
+    ("bf16", 4, 4, 128),   # one head per kv head: the four-wave kernel
+    ("bf16", 4, 4, 64),
+])
+def test_per_block_ring_equals_oracle_and_state(dtype, Hq, Hkv, D):
     # fp32 inputs follow the fp32 workload's recipe (N(0,1), logit std 1): with
     # a x8 head, fp32 accumulation of |q.k| ~ 400 alone costs ~1e-5 in out.
-    w = syn.scaled(SMALL, dtype=dtype, k_head_mul=SMALL.k_head_mul if dtype == "bf16" else None)
+    mul = tuple(8.0 if g % 2 else 1.0 for g in range(Hkv)) if dtype == "bf16" else None
+    w = syn.scaled(SMALL, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, k_head_mul=mul)
     inp = Inputs(w)
     rows = all_rows(w.B, w.Hq, w.C)
     starts, lens = np.arange(w.N) * w.C, np.full(w.N, w.C)
