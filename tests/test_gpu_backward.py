@@ -138,3 +138,21 @@ def test_backward_rows_without_keys():
         _check(f"dk[{o}:{o + l}]", gk, rk[:, o - 100:o - 100 + l])
         _check(f"dv[{o}:{o + l}]", gv, rv[:, o - 100:o - 100 + l])
     assert not dk[1].any() and not dv[1].any()
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_backward_one_head_per_kv_head(D):
+    """Hq = Hkv (no grouping): every dq workgroup covers four row blocks of one
+    head and every dk/dv query tile is one head's; causal, a diagonal block
+    that starts inside the query range, a full block, ragged lengths."""
+    q, k, v, dout = _seq(2, 3, 3, 650, D, 4005 + D)
+    q_off, Tq = 250, 400
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    ds = np.ascontiguousarray(dout[:, q_off:q_off + Tq])
+    blocks = [(250, 400), (0, 250)]
+    dq, dk, dv = _run(qs, k, v, ds, blocks, q_off, True)
+    rq, rk, rv = oracle.attention_backward(qs, k, v, ds, q_off=q_off, k_off=0, causal=True)
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
