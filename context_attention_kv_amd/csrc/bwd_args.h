@@ -8,7 +8,7 @@
 
 namespace cakv {
 
-constexpr int kBwdKeyTile = 128;   // keys per dK/dV workgroup (32 per wave)
+constexpr int kBwdKeyTile = 256;   // keys per dK/dV workgroup (32 per wave, 8 waves)
 
 // Gradients of the attention of Tq queries (global positions q_off + row)
 // against n_blocks key/value blocks, from the forward's out and lse.

@@ -19,13 +19,14 @@
 //   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 (K, V as A
 //   operands, Q^T and dO^T in registers as B), dS = P (dP - delta), then
 //   dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16.
-// bwd_dkdv_kernel: key-stationary, 4 waves of 32 keys (K^T in registers and
-//   the workgroup's 128 V rows in LDS, both B operands) over every 32-row
+// bwd_dkdv_kernel: key-stationary, 8 waves of 32 keys (K^T in registers and
+//   the workgroup's 256 V rows in LDS, both B operands) over every 32-row
 //   query tile of the kv head's query heads, copied into LDS: S = Q K^T and
 //   dP = dO V^T (query rows in output registers), dV^T += dO^T P and
 //   dK^T += Q^T dS with dO^T and Q^T read through ds_read_b64_tr_b16.
-// Both kernels fit two waves per SIMD (two workgroups per CU), so one
-// workgroup's products overlap the other's softmax work and barrier waits.
+// Both kernels run two waves per SIMD (dq: two 4-wave workgroups per CU; dk/dv:
+// one 8-wave workgroup, so that each query tile copied serves 256 keys), and
+// one wave's products overlap the other's softmax work and barrier waits.
 // Tile copies use buffer loads that write LDS directly: no staging registers,
 // and the range check of a per-tile buffer resource zero-fills rows past the
 // end of a block or of the query range.
@@ -407,10 +408,10 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dk, dv
 template <int D>
-__global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
+__global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     using C = BCfg<D>;
     constexpr int QR = 32, TB = QR * C::ROW_BYTES;
-    constexpr int NCP = TB / 1024 / 4;            // copies per wave per Q (or dO) tile
+    constexpr int REG = TB / 1024;                // 1 KB regions per Q (or dO) tile
     constexpr int VT = kBwdKeyTile * C::ROW_BYTES;   // the workgroup's V rows
     // [V rows] then 2 x [Q | dO | lse (64 floats) | delta (64 floats) | pad]
     constexpr int BUF = 2 * TB + 1024;
@@ -451,12 +452,12 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     }
     // the workgroup's V rows into LDS (swizzled tile; rows past the block's end zero)
     {
-        constexpr int PER = kBwdKeyTile * C::UNITS / 256;
+        constexpr int PER = kBwdKeyTile * C::UNITS / 512;
         const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) +
                             ((long long)b * len + wkey0) * kv_rs + (long long)g * D;
 #pragma unroll
         for (int n = 0; n < PER; ++n) {
-            const int c = tid + 256 * n;
+            const int c = tid + 512 * n;
             const int row = c / C::UNITS, p = c % C::UNITS;
             const u32x4 x = wkey0 + row < len ? *reinterpret_cast<const u32x4*>(vb_ + row * kv_rs + 8 * p)
                                               : u32x4{0u, 0u, 0u, 0u};
@@ -483,9 +484,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
     const int nq = (nrt - rt0) * G;   // query tiles to visit: (head, row block)
     // copy n of this wave fills 1 KB region 4n + wave of the Q and of the dO
     // tile; waves 0 and 1 also copy the tile's 32 lse and delta values
-    unsigned cp_off[NCP];
-#pragma unroll
-    for (int n = 0; n < NCP; ++n) cp_off[n] = region_off<D>(4 * n + wave, lane, q_rs);
+    const unsigned cp_off = region_off<D>(wave < REG ? wave : 0, lane, q_rs);
     // query tiles go head-fastest: tile n is head n % G of row block
     // rt0 + n / G; running counters instead of divisions
     int i_hj = 0, i_rt = rt0;   // the next tile to copy
@@ -501,10 +500,9 @@ __global__ void __launch_bounds__(256, 2) bwd_dkdv_kernel(const BwdArgs a) {
         const unsigned bytes = (unsigned)(rows * q_rs * 2);
         const i32x4 rq = make_rsrc(static_cast<const __bf16*>(a.q) + base, bytes);
         const i32x4 rd = make_rsrc(static_cast<const __bf16*>(a.dout) + base, bytes);
-#pragma unroll
-        for (int c = 0; c < NCP; ++c) {
-            copy16_to_lds(rq, cp_off[c], dst + (4 * c + wave) * 1024);
-            copy16_to_lds(rd, cp_off[c], dst + TB + (4 * c + wave) * 1024);
+        if (wave < REG) {   // wave w copies region w of the Q and of the dO tile
+            copy16_to_lds(rq, cp_off, dst + wave * 1024);
+            copy16_to_lds(rd, cp_off, dst + TB + wave * 1024);
         }
         if (wave < 2) {
             const long long si = ((long long)b * a.Hq + h) * a.Tq + r0;
@@ -655,7 +653,7 @@ int launch_all(const BwdArgs& a, void* stream) {
         if (e != hipSuccess) return (int)e;
     }
     if (n_kv > 0) {
-        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_kv), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_kv), dim3(512), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
