@@ -57,21 +57,23 @@ def _oracle_merged(q, k, v, blocks, q_off, causal, rows):
     return acc_o, acc_l
 
 
-def test_unequal_straddling_and_future_blocks_causal():
-    q, k, v = _seq(2, 8, 2, 2100, 128, "bf16", 3001)
+@pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 128), (4, 4, 128), (4, 4, 64)])
+def test_unequal_straddling_and_future_blocks_causal(Hq, Hkv, D):
+    # grouped heads at d=128 run the ping-pong kernel, the others the four-wave one
+    q, k, v = _seq(2, Hq, Hkv, 2100, D, "bf16", 3001)
     q_off, Tq = 1000, 300
     qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
     # straddles the query range / before it / wholly after it / straddles its
     # end / a short block; keys 1481..1999 are missing but no query sees them
     blocks = [(581, 700), (0, 517), (2000, 100), (1281, 200), (517, 64)]
     out, lse, tc = _run(qs, k, v, blocks, q_off, True, counters=True)
-    rows = all_rows(2, 8, Tq)
+    rows = all_rows(2, Hq, Tq)
     ro, rl = oracle.attention(qs, k, v, q_off=q_off, k_off=0, causal=True, rows=rows)
     go, gl = gather_rows(out, lse, rows)
     compare(go, gl, ro, rl, "bf16", "unequal / straddling / future blocks", rows)
     starts = np.array([o for o, _ in blocks])
     lens = np.array([l for _, l in blocks])
-    _, _, tiles = oracle.classify(Tq, q_off, starts, lens, causal=True, B=2, Hq=8,
+    _, _, tiles = oracle.classify(Tq, q_off, starts, lens, causal=True, B=2, Hq=Hq,
                                   tile_q=cakv.CAKV_TILE_Q, tile_k=cakv.CAKV_TILE_K)
     got = tc.cpu().numpy()
     say(f"  tiles: gpu {got[:2].tolist()} oracle {list(tiles)}")
