@@ -106,6 +106,17 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
 
 
+def forward_kernel_name(w) -> str:
+    """The forward kernel the library launches for this workload: fp32 inputs
+    go to the fp32 kernel; bf16 grouped-query shares at d=128 to the ping-pong
+    kernel, every other bf16 shape to the four-wave kernel."""
+    if w.dtype != "bf16":
+        return "fwd_f32_kernel"
+    if w.D == 64 or w.Hq == w.Hkv:
+        return "fwd_bf16_4w_kernel"
+    return "fwd_bf16_kernel"
+
+
 def bench_per_block(args):
     """One rank's share through the per-block ring-step calls, as a ring over
     several GPUs would drive them: cakv_state_init, then cakv_block_update for
@@ -186,7 +197,7 @@ def bench_per_block(args):
                    "chunk": C, "d_k": w.D, "causal": w.causal, "ranks": [r],
                    "calls": f"state_init + {len(blocks)} x block_update + finalize"},
         "roofline": {"bound": "mfma" if is_bf16 else "alu",
-                     "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
+                     "kernel": forward_kernel_name(w),
                      "achieved": round(tf, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                      "frac": round(tf / peak, 4), "traffic": None,
                      "avg_call_ms": round(ms, 4), "flops_per_call": flops},
@@ -477,7 +488,7 @@ def main():
     traffic = traffic_for(w.name)
     roofline = {
         "bound": "mfma" if is_bf16 else "alu",
-        "kernel": "fwd_bf16_kernel" if is_bf16 else "fwd_f32_kernel",
+        "kernel": forward_kernel_name(w),
         "achieved": round(achieved, 2),
         "peak": round(peak, 1),
         "unit": "TFLOP/s",
