@@ -40,9 +40,9 @@ def _seq(B, Hq, Hkv, T, D, seed):
     return q, k, v, dout
 
 
-def _check(name, got, ref):
+def _check(name, got, ref, floor=1e-3):
     d = np.abs(got.astype(np.float64) - ref)
-    rms = max(float(np.sqrt((ref ** 2).mean())), 1e-3)
+    rms = max(float(np.sqrt((ref ** 2).mean())), floor)
     st = dict(max=float(d.max()), mean=float(d.mean()), rms_ref=rms)
     say(f"  {name}: {st}")
     assert not np.isnan(got).any(), name
@@ -156,3 +156,87 @@ def test_backward_one_head_per_kv_head(D):
     for (o, l), gk, gv in zip(blocks, dk, dv):
         _check(f"dk[{o}:{o + l}]", gk, rk[:, o:o + l])
         _check(f"dv[{o}:{o + l}]", gv, rv[:, o:o + l])
+
+
+def test_backward_full_share_sampled():
+    """The backward at full size, in the launch configuration bench.py times
+    (the 131,072-token causal sequence, N = 8, rank 7's share of 16,384 rows,
+    32 query heads on 8 key/value heads, d = 128; workspace from
+    cakv_backward_workspace_size), checked where the oracle can compute
+    outputs one by one and by identities that hold at any size.
+
+    Sampled outputs (same bound as above): dq of the row runs [0, 4),
+    [8190, 8194) and [C-4, C) (each run's gradient needs only its own rows,
+    so the oracle takes those rows against every key); dk and dv of the last
+    four keys, positions 131,068..131,071, which only the last four query
+    rows see, so the oracle's run [C-4, C) gives their whole gradient.
+
+    Identities over every key (the outputs start as NaN, so every element
+    must be written): (i) each row's p sums to 1 over its keys, so
+    sum_j dv_j = sum over rows and grouped heads of dout, per kv head and
+    component. The kernels' bf16 p (rounding rms 2.3e-3 relative, summed
+    over ~1.2e5 keys with sum p^2 ~ e / Tk) and the fp32 lse leave about
+    1.2e-5 of sqrt(sum dout^2); bound 2e-4, while one key tile of 256
+    dropped or doubled moves the sum by ~2e-3. (ii) sum_j ds_ij = 0 for
+    every row (the delta term cancels the mean of dP under p), so
+    sum_j dk_j = 0; bf16 ds leaves ~3e-3 of the component's norm over keys
+    sqrt(sum_j dk_j^2); bound 5e-2, while leaving out delta gives ~1."""
+    w = syn.scaled(syn.WORKLOADS[5], name="backward-T131072-N8-Hq32-Hkv8-d128-bf16-causal",
+                   T=131072)
+    r, C, G = w.ranks[-1], w.C, w.Hq // w.Hkv
+    say(f"backward full share: {w.name} rank {r} C={C}")
+    k = syn.make_kv_full(w, "k")
+    v = syn.make_kv_full(w, "v")
+    q = syn.make_q_local(w, r)
+    dout = np.empty((w.B, C, w.Hq, w.D), np.uint16)
+    syn.fill(dout, seed=w.seed, tensor=7)
+    kd, vd, qd, dod = to_dev(k), to_dev(v), to_dev(q), to_dev(dout)
+    order = [(r - s) % w.N for s in range(w.N)]
+    kb = [kd[:, j * C:(j + 1) * C] for j in order]
+    vb = [vd[:, j * C:(j + 1) * C] for j in order]
+    offs = [j * C for j in order]
+    out = torch.empty((w.B, C, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.Hq, C), dtype=torch.float32, device="cuda")
+    cakv.cakv_forward_blocks(qd, kb, vb, offs, r * C, w.causal, out, lse)
+    dq = torch.full_like(out, float("nan"))
+    dk = [torch.full(t.shape, float("nan"), dtype=torch.float32, device="cuda") for t in kb]
+    dv = [torch.full(t.shape, float("nan"), dtype=torch.float32, device="cuda") for t in kb]
+    ws = torch.empty(cakv.cakv_backward_workspace_size(w.B, w.Hq, C) // 4, dtype=torch.float32,
+                     device="cuda")
+    cakv.cakv_backward_blocks(qd, kb, vb, offs, r * C, w.causal, out, lse, dod, dq, dk, dv,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    say("  gpu done")
+    dq = dq.cpu().numpy()
+    for t in dk + dv:
+        assert not torch.isnan(t).any().item()
+    assert not np.isnan(dq).any()
+
+    # sampled rows and the last keys against the oracle
+    for i0 in (0, 8190, C - 4):
+        qs = np.ascontiguousarray(q[:, i0:i0 + 4])
+        ds = np.ascontiguousarray(dout[:, i0:i0 + 4])
+        rq, rk, rv = oracle.attention_backward(qs, k, v, ds, q_off=r * C + i0, k_off=0,
+                                               causal=True)
+        _check(f"dq[{i0}:{i0 + 4}]", dq[:, i0:i0 + 4], rq)
+        if i0 == C - 4:
+            last = r * C + C - 4   # block order[0] == r holds positions r*C .. r*C + C - 1
+            # these gradients are ~3e-5 (p ~ 1 / Tk), so no floor on the scale
+            _check("dk[last 4 keys]", dk[0][:, C - 4:].cpu().numpy(), rk[:, last:last + 4], 0.0)
+            _check("dv[last 4 keys]", dv[0][:, C - 4:].cpu().numpy(), rv[:, last:last + 4], 0.0)
+        del rq, rk, rv
+
+    # identities over every key
+    sum_dk = sum(t.double().sum(dim=1) for t in dk).cpu().numpy()          # [B, Hkv, D]
+    norm_dk = np.sqrt(sum((t.double() ** 2).sum(dim=1) for t in dk).cpu().numpy())
+    sum_dv = sum(t.double().sum(dim=1) for t in dv).cpu().numpy()
+    do = dout.astype(np.uint32) << 16
+    do = do.view(np.float32).astype(np.float64).reshape(w.B, C, w.Hkv, G, w.D)
+    ref_dv = do.sum(axis=(1, 3))
+    scale_dv = np.sqrt((do ** 2).sum(axis=(1, 3)))
+    e_dv = float((np.abs(sum_dv - ref_dv) / scale_dv).max())
+    e_dk = float((np.abs(sum_dk) / norm_dk).max())
+    say(f"  sum_j dv_j vs sum dout: {e_dv:.3e} of sqrt(sum dout^2); "
+        f"|sum_j dk_j|: {e_dk:.3e} of the norm over keys")
+    assert e_dv <= 2e-4, e_dv
+    assert e_dk <= 5e-2, e_dk
