@@ -452,3 +452,24 @@ def test_o4_causal_future_keys_get_nothing():
     k2[0, 5] += 1.0                                           # key 5: seen by query 5 only
     dq2, _, _ = oracle.attention_backward(q, k2, v, dout, q_off=2, causal=True)
     assert np.array_equal(dq[0, :3], dq2[0, :3]) and not np.array_equal(dq[0, 3], dq2[0, 3])
+
+
+def test_o4_bf16_inputs_read_as_their_values():
+    """O4 on bf16 bit patterns (the GPU tests' inputs: q, k, v and dout all
+    bf16) equals O4 on fp32 arrays holding the same values, decoded by this
+    file's own bf16 decoder; also with the dtypes mixed, so each operand's
+    dtype flag is honoured on its own."""
+    rng = np.random.default_rng(46)
+    B, Tq, Tk, Hq, Hkv, D = 1, 5, 9, 4, 2, 8
+    bits = {n: _bf16_bits(rng.standard_normal(s).astype(np.float32))
+            for n, s in (("q", (B, Tq, Hq, D)), ("k", (B, Tk, Hkv, D)),
+                         ("v", (B, Tk, Hkv, D)), ("dout", (B, Tq, Hq, D)))}
+    vals = {n: np.vectorize(_bf16_value)(b).astype(np.float32) for n, b in bits.items()}
+    want = oracle.attention_backward(vals["q"], vals["k"], vals["v"], vals["dout"], q_off=4,
+                                     causal=True)
+    for mix in (("q", "k", "v", "dout"), ("q",), ("k", "v"), ("dout",)):
+        args = {n: (bits[n] if n in mix else vals[n]) for n in bits}
+        got = oracle.attention_backward(args["q"], args["k"], args["v"], args["dout"], q_off=4,
+                                        causal=True)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), mix
