@@ -116,3 +116,56 @@ def test_fp32_unequal_blocks_causal():
     ro, rl = oracle.attention(qs, k, v, q_off=q_off, k_off=0, causal=True, rows=rows)
     go, gl = gather_rows(out, lse, rows)
     compare(go, gl, ro, rl, "f32", "fp32 unequal blocks", rows)
+
+
+def _sweep_case(i):
+    """Seeded random shape: batch, head grouping, d, query offset and count,
+    and 1-5 blocks cut from [0, T) at random points, some dropped (gaps), an
+    empty one added now and then, in random order; every third case
+    bidirectional; in every fourth the block at position 0 is dropped, so
+    that early causal rows may see no key."""
+    rng = np.random.default_rng(5000 + i)
+    B = int(rng.integers(1, 3))
+    Hq, Hkv = [(1, 1), (2, 1), (4, 1), (4, 2), (4, 4), (8, 2), (6, 3)][int(rng.integers(0, 7))]
+    D = int(rng.choice([64, 128]))
+    T = int(rng.integers(64, 2500))
+    Tq = int(rng.integers(1, min(700, T) + 1))
+    q_off = int(rng.integers(0, T - Tq + 1))
+    causal = i % 3 != 2
+    nb = int(rng.integers(1, 6))
+    cuts = np.sort(rng.choice(np.arange(1, T), size=nb - 1, replace=False)) if nb > 1 else []
+    edges = [0, *[int(c) for c in cuts], T]
+    blocks = [(edges[j], edges[j + 1] - edges[j]) for j in range(nb)]
+    keep = [bl for bl in blocks if rng.random() < 0.8] or [blocks[-1]]
+    if i % 4 == 3 and len(keep) > 1:
+        keep = [bl for bl in keep if bl[0] != 0]
+    if rng.random() < 0.3:
+        keep.append((int(rng.integers(0, T)), 0))
+    order = rng.permutation(len(keep))
+    return B, Hq, Hkv, D, T, Tq, q_off, causal, [keep[j] for j in order]
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes_sweep(i):
+    """Sixteen seeded random shapes through cakv_forward_blocks (both bf16
+    kernels: grouped heads at d = 128 take the ping-pong kernel, the rest the
+    four-wave one), every row against the oracle's per-block attention
+    merged by log-sum-exp, and the tile counters against the brute-force
+    classification."""
+    B, Hq, Hkv, D, T, Tq, q_off, causal, blocks = _sweep_case(i)
+    say(f"sweep {i}: B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} Tq={Tq} q_off={q_off} "
+        f"causal={causal} blocks={blocks}")
+    q, k, v = _seq(B, Hq, Hkv, T, D, "bf16", 5000 + i)
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    out, lse, tc = _run(qs, k, v, blocks, q_off, causal, counters=True)
+    rows = all_rows(B, Hq, Tq)
+    ro, rl = _oracle_merged(qs, k, v, blocks, q_off, causal, rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", f"sweep {i}", rows)
+    starts = np.array([o for o, _ in blocks])
+    lens = np.array([l for _, l in blocks])
+    _, _, tiles = oracle.classify(Tq, q_off, starts, lens, causal=causal, B=B, Hq=Hq,
+                                  tile_q=cakv.CAKV_TILE_Q, tile_k=cakv.CAKV_TILE_K)
+    got = tc.cpu().numpy()
+    say(f"  tiles: gpu {got[:2].tolist()} oracle {list(tiles)}")
+    assert got[0] == tiles[0] and got[1] == tiles[1]
