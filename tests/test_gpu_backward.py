@@ -240,3 +240,69 @@ def test_backward_full_share_sampled():
         f"|sum_j dk_j|: {e_dk:.3e} of the norm over keys")
     assert e_dv <= 2e-4, e_dv
     assert e_dk <= 5e-2, e_dk
+
+
+def _bwd_sweep_case(i):
+    """Seeded random shape for the backward: batch, head grouping, d, query
+    offset and count. Causal cases cut the keys [k0, T) into 1-4 blocks at
+    random points (k0 inside the first half of the query range in every
+    fourth case, so that early rows see no key); bidirectional cases may
+    drop blocks (gaps); now and then an empty block; random order."""
+    rng = np.random.default_rng(6000 + i)
+    B = int(rng.integers(1, 3))
+    Hq, Hkv = [(1, 1), (2, 1), (4, 1), (4, 2), (4, 4), (8, 2), (6, 3)][int(rng.integers(0, 7))]
+    D = int(rng.choice([64, 128]))
+    T = int(rng.integers(64, 1500))
+    Tq = int(rng.integers(1, min(500, T) + 1))
+    q_off = int(rng.integers(0, T - Tq + 1))
+    causal = i % 2 == 0
+    k0 = int(rng.integers(0, q_off + Tq // 2 + 1)) if causal and i % 4 == 0 else 0
+    nb = int(rng.integers(1, 5))
+    cuts = (np.sort(rng.choice(np.arange(k0 + 1, T), size=min(nb - 1, T - k0 - 1), replace=False))
+            if nb > 1 else [])
+    edges = [k0, *[int(c) for c in cuts], T]
+    blocks = [(edges[j], edges[j + 1] - edges[j]) for j in range(len(edges) - 1)]
+    if not causal:
+        blocks = [bl for bl in blocks if rng.random() < 0.8] or [blocks[-1]]
+    if rng.random() < 0.3:
+        blocks.append((int(rng.integers(k0, T)), 0))
+    order = rng.permutation(len(blocks))
+    return B, Hq, Hkv, D, T, Tq, q_off, causal, k0, [blocks[j] for j in order]
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_backward_random_shapes_sweep(i):
+    """Eight seeded random shapes through cakv_backward_blocks against O4.
+    The oracle takes one key sequence: causal cases give it the contiguous
+    keys [k0, T) at their positions; bidirectional ones, where positions do
+    not matter, the blocks' keys concatenated. Each block's dk, dv are
+    compared with the matching rows of the oracle's."""
+    B, Hq, Hkv, D, T, Tq, q_off, causal, k0, blocks = _bwd_sweep_case(i)
+    say(f"backward sweep {i}: B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} Tq={Tq} q_off={q_off} "
+        f"causal={causal} blocks={blocks}")
+    q, k, v, _ = _seq(B, Hq, Hkv, T, D, 6000 + i)
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    dout = np.empty((B, Tq, Hq, D), np.uint16)
+    syn.fill(dout, seed=6000 + i, tensor=7)
+    dq, dk, dv = _run(qs, k, v, dout, blocks, q_off, causal)
+    if causal:
+        at = {bl: bl[0] - k0 for bl in blocks}
+        ks, vs, k_off = np.ascontiguousarray(k[:, k0:]), np.ascontiguousarray(v[:, k0:]), k0
+    else:
+        nz = sorted(bl for bl in blocks if bl[1] > 0)
+        at, pos = {}, 0
+        for bl in nz:
+            at[bl] = pos
+            pos += bl[1]
+        ks = np.ascontiguousarray(np.concatenate([k[:, o:o + l] for o, l in nz], axis=1))
+        vs = np.ascontiguousarray(np.concatenate([v[:, o:o + l] for o, l in nz], axis=1))
+        k_off = 0
+    rq, rk, rv = oracle.attention_backward(qs, ks, vs, dout, q_off=q_off, k_off=k_off,
+                                           causal=causal)
+    _check("dq", dq, rq)
+    for (o, l), gk, gv in zip(blocks, dk, dv):
+        if l == 0:
+            continue
+        s = at[(o, l)]
+        _check(f"dk[{o}:{o + l}]", gk, rk[:, s:s + l])
+        _check(f"dv[{o}:{o + l}]", gv, rv[:, s:s + l])
