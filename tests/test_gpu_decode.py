@@ -150,3 +150,46 @@ def test_decode_million_token_history_all_rows():
     ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=True, rows=rows)
     go, gl = gather_rows(out, lse, rows)
     compare(go, gl, ro, rl, "bf16", "decode million-token history", rows)
+
+
+def _decode_sweep_case(i):
+    """Seeded random decode shape: batch, head grouping, d, history length,
+    1-16 new tokens, and the whole sequence's keys cut into 1-6 portions at
+    random points, some dropped (gaps), now and then an empty one, in random
+    order; every third case bidirectional."""
+    rng = np.random.default_rng(7000 + i)
+    B = int(rng.integers(1, 3))
+    Hq, Hkv = [(1, 1), (4, 1), (4, 2), (8, 2), (6, 3), (32, 8)][int(rng.integers(0, 6))]
+    D = int(rng.choice([64, 128]))
+    hist = int(rng.integers(1, 5000))
+    Tn = int(rng.integers(1, 17))
+    causal = i % 3 != 2
+    total = hist + Tn
+    nb = int(rng.integers(1, 7))
+    cuts = (np.sort(rng.choice(np.arange(1, total), size=min(nb - 1, total - 1), replace=False))
+            if nb > 1 else [])
+    edges = [0, *[int(c) for c in cuts], total]
+    bounds = [(edges[j], edges[j + 1] - edges[j]) for j in range(len(edges) - 1)]
+    bounds = [bd for bd in bounds if rng.random() < 0.8] or [bounds[-1]]
+    if rng.random() < 0.3:
+        bounds.append((int(rng.integers(0, total)), 0))
+    order = rng.permutation(len(bounds))
+    return B, Hq, Hkv, D, hist, Tn, causal, [bounds[j] for j in order]
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_decode_random_shapes_sweep(i):
+    """Eight seeded random decode shapes through cakv_decode, every row
+    against the oracle's per-portion attention merged by log-sum-exp."""
+    B, Hq, Hkv, D, hist, Tn, causal, bounds = _decode_sweep_case(i)
+    say(f"decode sweep {i}: B={B} Hq={Hq} Hkv={Hkv} D={D} hist={hist} Tn={Tn} "
+        f"causal={causal} portions={bounds}")
+    w = syn.DecodeWorkload("decode-sweep", B=B, Hq=Hq, Hkv=Hkv, hist=hist, N=1, Tn=Tn, D=D,
+                           causal=causal, seed=7000 + i)
+    q, k, v = syn.make_decode(w)
+    kp, vp = _portions_dev(k, v, bounds)
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], hist, causal)
+    rows = all_rows(B, Hq, Tn)
+    ro, rl = _oracle_by_portions(q, k, v, bounds, hist, causal, rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", f"decode sweep {i}", rows)
