@@ -169,3 +169,19 @@ def test_random_shapes_sweep(i):
     got = tc.cpu().numpy()
     say(f"  tiles: gpu {got[:2].tolist()} oracle {list(tiles)}")
     assert got[0] == tiles[0] and got[1] == tiles[1]
+
+
+@pytest.mark.parametrize("i", range(100, 106))
+def test_random_shapes_sweep_fp32(i):
+    """Six more seeded random shapes with fp32 inputs (the fp32 kernel),
+    every row against the oracle to the fp32 tolerances."""
+    B, Hq, Hkv, D, T, Tq, q_off, causal, blocks = _sweep_case(i)
+    say(f"fp32 sweep {i}: B={B} Hq={Hq} Hkv={Hkv} D={D} T={T} Tq={Tq} q_off={q_off} "
+        f"causal={causal} blocks={blocks}")
+    q, k, v = _seq(B, Hq, Hkv, T, D, "f32", 5000 + i)
+    qs = np.ascontiguousarray(q[:, q_off:q_off + Tq])
+    out, lse, _ = _run(qs, k, v, blocks, q_off, causal)
+    rows = all_rows(B, Hq, Tq)
+    ro, rl = _oracle_merged(qs, k, v, blocks, q_off, causal, rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "f32", f"fp32 sweep {i}", rows)
