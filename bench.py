@@ -44,6 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "fwd_bf16.hip")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "decode_bf16.hip")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "backward_traffic.json")
+BWD_SRC = os.path.join(ROOT, "context_attention_kv_amd", "csrc", "bwd_bf16.hip")
 
 
 def log(msg):
@@ -88,6 +90,19 @@ def decode_traffic(workload_name: str):
     except (OSError, ValueError):
         return None
     if rec.get("kernel_sha") != kernel_hash(DECODE_SRC) or rec.get("workload") != workload_name:
+        return None
+    return rec.get("bytes_per_call")
+
+
+def backward_traffic(workload_name: str):
+    """HBM bytes per backward call (delta, dq and dk/dv kernels) from the
+    committed counter profile, if taken on this workload and the current
+    kernel source."""
+    try:
+        rec = json.load(open(BWD_TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_hash(BWD_SRC) or rec.get("workload") != workload_name:
         return None
     return rec.get("bytes_per_call")
 
@@ -284,7 +299,8 @@ def bench_backward(args):
                    "chunk": C, "d_k": w.D, "causal": w.causal, "ranks": [r]},
         "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel + bwd_dkdv_kernel (+ bwd_delta)",
                      "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": backward_traffic(w.name),
                      "avg_call_ms": round(ms, 4), "flops_per_call": flops},
     }
     print(json.dumps(rec), flush=True)
