@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
     float* ks = smem + wave * 2 * C::STAGE;   // this wave's K and V tile
     float* vs = ks + C::STAGE;
 
-    // tiles in block order, kBK keys at a time; round r gives tile 4r + w to wave w
+    // tiles in block order, kBK keys at a time; step r gives tile 4r + w to wave w
     int t = 0, key0 = 0, need = 0;
     auto settle = [&]() {   // move (t, key0) to the next tile that exists
         while (t < a.n_blocks && key0 >= need) {
@@ -95,7 +95,7 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
     if (a.n_blocks > 0) need = keys_needed(a, 0, last_pos);
     settle();
     while (t < a.n_blocks) {
-        // this round's tile for this wave: skip `wave` tiles ahead
+        // this wave's tile of the current group of kWaves tiles: skip `wave` tiles ahead
         int mt = t, mk = key0, mneed = need;
         for (int s = 0; s < wave && mt < a.n_blocks; ++s) {
             mk += kBK;
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
                 m_run = m_new;
             }
         }
-        // next round: four tiles on
+        // next step: four tiles on
         for (int s = 0; s < kWaves && t < a.n_blocks; ++s) {
             key0 += kBK;
             settle();
