@@ -121,6 +121,83 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi GPU metrics) from a host thread
+    while the timed steps run, so the line can say at what clock the chip ran
+    (the matrix cores' rate follows it, and it varies from box to box under
+    the board's power limit). Reports nothing where amdsmi is not usable."""
+
+    def __init__(self, period_s: float = 0.05):
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        self._read = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def read():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                for key in ("current_gfxclk", "average_gfxclk_frequency"):
+                    v = m.get(key)
+                    if isinstance(v, (int, float)) and 0 < v < 10000:
+                        return float(v)
+                vals = [x for x in (m.get("current_gfxclks") or [])
+                        if isinstance(x, (int, float)) and 0 < x < 10000]
+                if vals:
+                    return float(sum(vals)) / len(vals)
+                c = amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
+                return float(c.get("clk", c.get("cur_clk")))
+
+            read()
+            self._read = read
+        except Exception as e:   # noqa: BLE001 -- optional telemetry
+            log(f"clock sampling unavailable: {type(e).__name__}: {e}")
+
+    def __enter__(self):
+        if self._read is None:
+            return self
+        import threading
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception:   # noqa: BLE001
+                    pass
+                self._stop.wait(self.period)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"median_MHz": xs[len(xs) // 2], "min_MHz": xs[0], "max_MHz": xs[-1],
+                "samples": len(xs), "source": "amdsmi GPU metrics, sampled every 50 ms "
+                                              "during the timed steps"}
+
+
+def launch_stats(ms):
+    """median / min / max / mean of the per-launch HIP-event times (ms)."""
+    xs = sorted(ms)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"median": round(med, 4), "min": round(xs[0], 4), "max": round(xs[-1], 4),
+            "mean": round(sum(xs) / n, 4), "n": n}
+
+
 def forward_kernel_name(w) -> str:
     """The forward kernel the library launches for this workload: fp32 inputs
     go to the fp32 kernel; bf16 grouped-query shares at d=128 to the ping-pong
@@ -485,11 +562,13 @@ def main():
         torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        step(s)
-    torch.cuda.synchronize()
-    t_end = time.perf_counter()
+    clock = ClockSampler()
+    with clock:
+        t_start = time.perf_counter()
+        for s in range(args.steps):
+            step(s)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
     log("timed steps done")
 
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
@@ -499,6 +578,9 @@ def main():
     # per-launch useful FLOPs: each launch is one rank's shard
     per_launch = [useful_flops(w, [r]) for r in ranks] * args.steps
     achieved = sum(per_launch) / (sum(launch_ms) * 1e-3) / 1e12
+    # per-step launch time (all ranks' launches of a step summed)
+    step_ms = [sum(launch_ms[i * n_launch:(i + 1) * n_launch]) for i in range(args.steps)]
+    st = launch_stats(step_ms)
     is_bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if is_bf16 else PEAK_F32_VALU_TFLOPS
     traffic = traffic_for(w.name)
@@ -512,6 +594,12 @@ def main():
         "traffic": traffic,
         "avg_launch_ms": round(sum(launch_ms) / len(launch_ms), 4),
         "flops_per_launch": per_launch[0] if len(set(per_launch)) == 1 else None,
+        # the same rate from the median / fastest / slowest timed step
+        "launch_ms": st,
+        "achieved_median": round(flops_step / (st["median"] * 1e-3) / 1e12, 2),
+        "achieved_range": [round(flops_step / (st["max"] * 1e-3) / 1e12, 2),
+                           round(flops_step / (st["min"] * 1e-3) / 1e12, 2)],
+        "gfx_clock": clock.summary(),
     }
 
     # ---- what the matrix cores sustain on this chip (bf16 workloads) -------

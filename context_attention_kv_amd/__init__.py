@@ -124,6 +124,17 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _counters(tc) -> Optional[int]:
+    """Device pointer of a tile-counter tensor: int64 with the three entries
+    (full, masked, skipped) the library adds to."""
+    if tc is None:
+        return None
+    import torch
+    if tc.dtype != torch.int64 or tc.numel() < 3 or not tc.is_contiguous():
+        raise ValueError("tile_counters must be a contiguous int64 tensor of 3 entries")
+    return tc.data_ptr()
+
+
 def abi_version() -> int:
     return _lib.cakv_abi_version()
 
@@ -166,7 +177,7 @@ def cakv_block_update(q, k, v, q_offset: int, kv_offset: int, causal: bool, m, l
         raise ValueError("state shapes disagree with q")
     _check(_lib.cakv_block_update(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, Tq,
                                   Tkv, D, q_offset, kv_offset, int(causal), float(scale),
-                                  _ptr(m), _ptr(l), _ptr(o), _ptr(tile_counters),
+                                  _ptr(m), _ptr(l), _ptr(o), _counters(tile_counters),
                                   _stream(stream)), "cakv_block_update")
 
 
@@ -208,7 +219,7 @@ def cakv_local_shard_forward(q_local, k_blocks: Sequence, v_blocks: Sequence, ra
     _check(_lib.cakv_local_shard_forward(_ptr(q_local), karr, varr, _dtype_code(q_local), B,
                                          Hq, Hkv, C, n, D, rank, int(causal), float(scale),
                                          _ptr(out), _dtype_code(out), _ptr(lse),
-                                         _ptr(tile_counters), _stream(stream)),
+                                         _counters(tile_counters), _stream(stream)),
            "cakv_local_shard_forward")
 
 
@@ -291,7 +302,7 @@ def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: S
     oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
     _check(_lib.cakv_forward_blocks(_ptr(q), karr, varr, larr, oarr, n, _dtype_code(q), B, Hq,
                                     Hkv, Tq, D, int(q_offset), int(causal), float(scale),
-                                    _ptr(out), _dtype_code(out), _ptr(lse), _ptr(tile_counters),
+                                    _ptr(out), _dtype_code(out), _ptr(lse), _counters(tile_counters),
                                     _stream(stream)), "cakv_forward_blocks")
 
 

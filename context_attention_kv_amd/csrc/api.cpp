@@ -218,7 +218,18 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
         return fail(CAKV_ERR_ALIGN, "q, k, v and o must be 16-byte aligned");
     if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
         return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
-    if (classify(q_offset, Tq, kv_offset, Tkv, causal) == CAKV_SKIP) return ok();
+    if (classify(q_offset, Tq, kv_offset, Tkv, causal) == CAKV_SKIP) {
+        if (!tile_counters) return ok();
+        // nothing to compute: every tile of the block is skipped
+        const unsigned long long tiles = (unsigned long long)B * Hq *
+                                         (unsigned long long)((Tq + CAKV_TILE_Q - 1) / CAKV_TILE_Q) *
+                                         (unsigned long long)((Tkv + CAKV_TILE_K - 1) / CAKV_TILE_K);
+        if (tiles == 0) return ok();
+        return hip_status(cakv::launch_counter_add(
+                              reinterpret_cast<unsigned long long*>(tile_counters) + 2, tiles,
+                              stream),
+                          "block_update counter launch");
+    }
 
     cakv::FwdArgs a;
     std::memset(&a, 0, sizeof a);
@@ -301,7 +312,10 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     std::memset(&a, 0, sizeof a);
     int n = 0;
     for (int t = 0; t < n_chunks; ++t) {
-        if (cls[t] == CAKV_SKIP) continue;
+        if (cls[t] == CAKV_SKIP) {
+            a.skip_tiles += (chunk_len + CAKV_TILE_K - 1) / CAKV_TILE_K;
+            continue;
+        }
         const int j = order[t];
         const void* kp = k_blocks_host[j];
         const void* vp = v_blocks_host[j];
@@ -359,7 +373,10 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     std::memset(&a, 0, sizeof a);
     int n = 0;
     for (int t = 0; t < n_blocks; ++t) {
-        if (classify(q_offset, Tq, kv_off_host[t], kv_len_host[t], causal) == CAKV_SKIP) continue;
+        if (classify(q_offset, Tq, kv_off_host[t], kv_len_host[t], causal) == CAKV_SKIP) {
+            a.skip_tiles += (kv_len_host[t] + CAKV_TILE_K - 1) / CAKV_TILE_K;
+            continue;
+        }
         const void* kp = k_blocks_host[t];
         const void* vp = v_blocks_host[t];
         if (!kp || !vp) return fail(CAKV_ERR_NULL, "block %d pointer is NULL", t);

@@ -30,7 +30,9 @@ struct FwdArgs {
     void* out;                            // [B, Tq, Hq, D], fp32 or bf16
     int out_bf16;
     float* lse;                           // [B, Hq, Tq] or null
-    unsigned long long* counters;         // [2] full / masked tiles, or null
+    unsigned long long* counters;         // [3] full / masked / skipped tiles, or null
+    long long skip_tiles;                 // CAKV_TILE_K-key tiles of blocks dropped from the
+                                          // list as SKIP, per 32-row tile (counters only)
     int wg_per_bg;                        // workgroups per (batch, kv head)
     int n_wg;                             // total workgroups
 };
@@ -42,6 +44,7 @@ int fwd_bf16_waves(int D, int G);   // waves per workgroup (32 query rows each) 
 int fwd_f32_wg_rows();
 
 int launch_state_init(float* m, float* l, float* o, long long rows, int D, void* stream);
+int launch_counter_add(unsigned long long* counter, unsigned long long value, void* stream);
 int launch_mfma_burn(int zero, int iters, float* sink, void* stream);
 int launch_finalize(const float* m, const float* l, const float* o, void* out, int out_bf16,
                     float* lse, int B, int Hq, int Tq, int D, void* stream);

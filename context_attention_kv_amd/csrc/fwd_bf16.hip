@@ -219,7 +219,18 @@ __device__ __forceinline__ void cursor_next(const FwdArgs& a, const HeadAt& at, 
     }
 }
 
-// COUNT: tally the tiles each wave computes (full / masked) into a.counters
+// Tiles (64 keys) that a workgroup whose tile sequence has T tiles never
+// visits: whole blocks after its last query (causal), the tails of blocks
+// past it, and the tiles of blocks the host's schedule left out of the list.
+// For each of its waves these are skipped tiles.
+__device__ __forceinline__ unsigned skipped_unvisited(const FwdArgs& a, int T) {
+    long long all = a.skip_tiles;
+    for (int t = 0; t < a.n_blocks; ++t) all += (a.kv_len[t] + kBK - 1) / kBK;
+    return (unsigned)(all - T);
+}
+
+// COUNT: tally the tiles of each wave's rows (computed full / masked, skipped)
+// into a.counters
 template <int D, bool COUNT>
 __global__ void __launch_bounds__(512)
 fwd_bf16_kernel(const FwdArgs a) {
@@ -325,12 +336,14 @@ fwd_bf16_kernel(const FwdArgs a) {
     // form the compiler's wait tracking understands, so that no wait for them
     // lands inside the loop (where it would also wait for the tile copies).
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    unsigned n_full = 0, n_masked = 0;   // tiles this wave computed, unmasked / masked
+    // tiles of this wave's rows: computed unmasked / masked, and skipped
+    unsigned n_full = 0, n_masked = 0, n_skip = 0;
 
     // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
     const HeadAt at{b, g, kv_rs, D, wg_last_pos, wave_first_pos, a.causal};
     int T = 0;
     for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
+    if constexpr (COUNT) n_skip = wave_valid ? skipped_unvisited(a, T) : 0u;
 
     // Tile copies: the first group copies K tiles, the second V tiles, each
     // two tiles ahead, into a ring of NB buffers [K | V].
@@ -467,6 +480,7 @@ fwd_bf16_kernel(const FwdArgs a) {
         if constexpr (COUNT) {
             n_full += cmp && full ? 1u : 0u;
             n_masked += cmp && !full ? 1u : 0u;
+            n_skip += t < T && wave_valid && !cmp ? 1u : 0u;
         }
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
@@ -602,9 +616,10 @@ fwd_bf16_kernel(const FwdArgs a) {
             }
         }
     }
-    if (COUNT && lane == 0 && (n_full | n_masked)) {
+    if (COUNT && lane == 0 && (n_full | n_masked | n_skip)) {
         atomicAdd(a.counters + 0, (unsigned long long)n_full);
         atomicAdd(a.counters + 1, (unsigned long long)n_masked);
+        atomicAdd(a.counters + 2, (unsigned long long)n_skip);
     }
 }
 
@@ -709,12 +724,13 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     const int v_sw = vswz<D>(src >> 2);
 
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the Q and state loads
-    unsigned n_full = 0, n_masked = 0;
+    unsigned n_full = 0, n_masked = 0, n_skip = 0;
 
     // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
     const HeadAt at{b, g, kv_rs, D, wg_last_pos, wave_first_pos, a.causal};
     int T = 0;
     for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
+    if constexpr (COUNT) n_skip = wave_valid ? skipped_unvisited(a, T) : 0u;
 
     // Tile copies: copy n of every wave fills 1 KB region 4n + wave of the K
     // and of the V tile.
@@ -783,6 +799,7 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
         if constexpr (COUNT) {
             n_full += cmp && full ? 1u : 0u;
             n_masked += cmp && !full ? 1u : 0u;
+            n_skip += wave_valid && !cmp ? 1u : 0u;
         }
         if (cmp) {
             // S^T = K Q^T : s[kb][r] = score(query row0 + l32, key key0 + 32kb + 16hh + r)
@@ -914,9 +931,10 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
             }
         }
     }
-    if (COUNT && lane == 0 && (n_full | n_masked)) {
+    if (COUNT && lane == 0 && (n_full | n_masked | n_skip)) {
         atomicAdd(a.counters + 0, (unsigned long long)n_full);
         atomicAdd(a.counters + 1, (unsigned long long)n_masked);
+        atomicAdd(a.counters + 2, (unsigned long long)n_skip);
     }
 }
 

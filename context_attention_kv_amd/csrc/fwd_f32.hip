@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
 #pragma unroll
         for (int c = 0; c < D; ++c) o[c] = a.o[oi + c];
     }
-    unsigned long long n_full = 0, n_masked = 0;
+    unsigned long long n_full = 0, n_masked = 0, n_skip = 0;
     float* ks = smem + wave * 2 * C::STAGE;   // this wave's K and V tile
     float* vs = ks + C::STAGE;
 
@@ -139,6 +139,7 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
                     const long long p0 = a.q_off + r0, p1 = a.q_off + min(r0 + 32, a.Tq) - 1;
                     if (!a.causal || c_last <= p0) ++n_full;
                     else if (kpos0 <= p1) ++n_masked;
+                    else ++n_skip;
                 }
             }
             const bool need_mask = (a.causal && kpos_last > first_pos) || tile_keys < kBK;
@@ -233,9 +234,20 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
             }
         }
     }
-    if (a.counters && lane == 0 && (n_full | n_masked)) {
+    if (a.counters && lane == 0 && wave == 0) {
+        // counted tiles of blocks (or block tails) past the workgroup's last
+        // query, which no wave visits, and of blocks the host's schedule left
+        // out of the list: skipped for each of its slabs
+        long long unvisited = a.skip_tiles;
+        for (int t = 0; t < a.n_blocks; ++t)
+            unvisited += (a.kv_len[t] + kCountKeys - 1) / kCountKeys -
+                         (keys_needed(a, t, last_pos) + kCountKeys - 1) / kCountKeys;
+        n_skip += (unsigned long long)unvisited * (unsigned long long)((wg_rows + 31) / 32);
+    }
+    if (a.counters && lane == 0 && (n_full | n_masked | n_skip)) {
         atomicAdd(a.counters + 0, n_full);
         atomicAdd(a.counters + 1, n_masked);
+        atomicAdd(a.counters + 2, n_skip);
     }
 }
 

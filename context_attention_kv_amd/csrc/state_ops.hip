@@ -40,6 +40,12 @@ init_kernel(float* __restrict__ m, float* __restrict__ l, float* __restrict__ o,
     }
 }
 
+// Adds `value` to one tile counter: the tiles of a block that the schedule
+// skips as a whole (nothing else is launched for it).
+__global__ void counter_add_kernel(unsigned long long* counter, unsigned long long value) {
+    if (threadIdx.x == 0) atomicAdd(counter, value);
+}
+
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 finalize_kernel(const float* m, const float* l, const float* o, void* out, int out_bf16,
@@ -114,6 +120,12 @@ int launch_state_init(float* m, float* l, float* o, long long rows, int D, void*
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(init_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), m, l, o, rows, D);
+    return (int)hipGetLastError();
+}
+
+int launch_counter_add(unsigned long long* counter, unsigned long long value, void* stream) {
+    hipLaunchKernelGGL(counter_add_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       counter, value);
     return (int)hipGetLastError();
 }
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define CAKV_ABI_VERSION 1
+#define CAKV_ABI_VERSION 2 /* 2: tile_counters holds three counts */
 #define CAKV_MAX_CHUNKS 64 /* most key/value blocks one forward call takes */
 #define CAKV_TILE_Q 32     /* query rows per counted tile */
 #define CAKV_TILE_K 64     /* keys per counted tile */
@@ -126,8 +126,15 @@ cakv_status cakv_schedule(int rank, int n_chunks, int64_t chunk_len, int causal,
                           int32_t* blocks_host, int8_t* class_host);
 
 /*
- * Empty running state for B*Hq*Tq rows: m = -inf, l = 0, o = 0.
- * m, l: [B, Hq, Tq] fp32; o: [B, Tq, Hq, D] fp32.
+ * Empty running state for B*Hq*Tq rows: m = -inf, l = 0, o = 0, the state
+ * before the first block of the running update of page section "But softmax
+ * seems to require all attention scores at once" (the page leaves the
+ * starting values implicit; these are the ones for which folding the first
+ * block gives that block's own m, l, o).
+ * m, l: [B, Hq, Tq] fp32; o: [B, Tq, Hq, D] fp32, 16-byte aligned.
+ * Errors: negative sizes, D not 64 or 128 (CAKV_ERR_SHAPE); NULL state
+ * pointers (CAKV_ERR_NULL) or a misaligned o (CAKV_ERR_ALIGN) when there is
+ * at least one row. Zero rows returns CAKV_OK and launches nothing.
  */
 cakv_status cakv_state_init(float* m, float* l, float* o, int B, int Hq, int Tq, int D,
                             void* stream);
@@ -139,11 +146,15 @@ cakv_status cakv_state_init(float* m, float* l, float* o, int B, int Hq, int Tq,
  * k, v: [B, Tkv, Hkv, D] keys/values at global positions kv_offset + row;
  * dtype: CAKV_BF16 or CAKV_F32 (q, k, v share it); scale <= 0 -> 1/sqrt(D).
  * m, l, o: running state, read and written in place.
- * tile_counters (nullable, device int64[2]): the call ADDS the number of
- * (CAKV_TILE_Q rows x CAKV_TILE_K keys) tiles, per batch row and query head,
- * that it computed unmasked [0] and masked [1]; tiles of CAKV_SKIP class are
- * not computed and not counted. A block with no allowed pair (CAKV_SKIP)
- * returns CAKV_OK and launches nothing.
+ * tile_counters (nullable, device int64[3]): the call ADDS the number of
+ * (CAKV_TILE_Q rows x CAKV_TILE_K keys) tiles of the block's grid, summed
+ * over batch rows and query heads, that it computed unmasked [0], computed
+ * masked [1] and skipped [2] (no allowed pair: never read); the three add up
+ * to the whole grid (page section "Causal attention gives us another
+ * optimization": fully masked work is not done, only the diagonal is
+ * masked). A block with no allowed pair (CAKV_SKIP) returns CAKV_OK and
+ * launches nothing, or, when counters are given, only a one-thread kernel
+ * that adds its tiles to [2].
  */
 cakv_status cakv_block_update(const void* q, const void* k, const void* v, int dtype,
                               int B, int Hq, int Hkv, int Tq, int Tkv, int D,
@@ -153,8 +164,16 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
 
 /*
  * out = o / l (fp32, or bf16 if out_dtype == CAKV_BF16) and lse = m + ln(l)
- * (fp32); rows with l == 0 give out = 0, lse = -inf. out may alias o when
- * out_dtype is CAKV_F32. lse may be NULL.
+ * (fp32); rows with l == 0 give out = 0, lse = -inf. Page section "But
+ * softmax seems to require all attention scores at once": o holds the
+ * e^{s - m}-weighted sum of values and l the sum of the weights, so the
+ * softmax output is their ratio (the page stops before this division; it is
+ * the plain reading of an unnormalised accumulator), and m + ln(l) is the
+ * log of the row's whole softmax denominator, the quantity partial results
+ * are combined by. m, l: [B, Hq, Tq]; o, out: [B, Tq, Hq, D], 16-byte
+ * aligned; out may alias o when out_dtype is CAKV_F32. lse may be NULL.
+ * Errors: unknown out_dtype (CAKV_ERR_DTYPE); sizes as cakv_state_init;
+ * NULL m, l, o or out (CAKV_ERR_NULL); misaligned o / out (CAKV_ERR_ALIGN).
  */
 cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* out,
                           int out_dtype, float* lse, int B, int Hq, int Tq, int D,
@@ -176,15 +195,21 @@ cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_
 
 /*
  * One rank's whole share: attention of the stationary local queries q_local
- * (chunk `rank`, global positions rank*chunk_len + row) against the
- * n_chunks key/value blocks, consumed in ring order rank, rank-1, ...
- * (cakv_schedule), SKIP blocks never read, then finalised. The running state
- * stays on chip for the whole ring; nothing but out and lse is written.
+ * (chunk `rank`, global positions rank*chunk_len + row; page section "Split
+ * tokens across four GPUs") against the n_chunks key/value blocks, consumed
+ * in ring order rank, rank-1, ... (cakv_schedule; page section "A better
+ * mental model: move blocks past the queries"), each folded by the running
+ * update of section "But softmax seems to require all attention scores at
+ * once", SKIP blocks never read and only DIAG tiles masked (section "Causal
+ * attention gives us another optimization"), then finalised as
+ * cakv_finalize. The running state stays on chip for the whole ring; nothing
+ * but out and lse is written.
  * q_local: [B, chunk_len, Hq, D];
  * k_blocks_host, v_blocks_host: HOST arrays of n_chunks device pointers,
  *   block j = [B, chunk_len, Hkv, D] holding positions [j*chunk_len, ...);
  * out: [B, chunk_len, Hq, D] in out_dtype; lse: [B, Hq, chunk_len] fp32
- *   (nullable); tile_counters: as for cakv_block_update (nullable).
+ *   (nullable); tile_counters: as for cakv_block_update, over the grids of
+ *   all n_chunks blocks (nullable).
  * Errors: as above plus rank outside [0, n_chunks), n_chunks outside
  * [1, CAKV_MAX_CHUNKS], a NULL block pointer that the schedule would read.
  */

@@ -1,9 +1,9 @@
 """Helpers shared by the GPU tests: device upload of seeded host inputs, the
 ring call through the C ABI, and comparison against the fp64 oracle.
 
-Tolerances (fp32 output vs the fp64 oracle on the same inputs):
-  bf16 inputs, fp32 accumulation: max |d out| <= 1e-2, mean |d out| <= 1e-3,
-  fp32 inputs: max |d out| <= 1e-5; every row: |d lse| <= 1e-3.
+Tolerances (tests/tolerances.py): absolute bounds on out and lse, and a
+scale-aware per-row bound max_c |d out| / rms(out_ref row) that still bites
+where |out| is ~1e-3 (a million keys of U(-1,1) values).
 """
 from __future__ import annotations
 
@@ -15,11 +15,7 @@ import torch
 import cakv_synth as syn
 import context_attention_kv_amd as cakv
 import oracle
-
-TOL = {
-    "bf16": dict(max_out=1e-2, mean_out=1e-3, lse=1e-3),
-    "f32": dict(max_out=1e-5, mean_out=1e-5, lse=1e-3),
-}
+from tolerances import TOL, check_rel, row_rel_errors
 
 
 def say(msg: str):
@@ -93,27 +89,34 @@ def all_rows(B, H, T):
     return np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int64)
 
 
-def compare(got_o, got_l, ref_o, ref_l, dtype: str, what: str, rows=None):
-    """Assert the tolerances; returns the error statistics. `rows` (b, h, i)
-    only labels the worst rows in the log."""
+def compare(got_o, got_l, ref_o, ref_l, dtype: str, what: str, rows=None, out_bf16=False):
+    """Assert the tolerances (absolute and per-row relative); returns the
+    error statistics. `rows` (b, h, i) only labels the worst rows in the log;
+    out_bf16 marks a bf16 output copy (its own rounding widens the relative
+    bound)."""
     tol = TOL[dtype]
+    rel_kind = "f32" if dtype == "f32" else ("bf16-out" if out_bf16 else "bf16")
+    rel_ok, rel_max, rel_mean = check_rel(got_o, ref_o, rel_kind)
     d = np.abs(got_o - ref_o)
     fin = np.isfinite(ref_l)
     assert np.array_equal(fin, np.isfinite(got_l)), f"{what}: lse finiteness differs"
     dl = np.abs(got_l[fin] - ref_l[fin]) if fin.any() else np.zeros(1)
     stats = dict(max_out=float(d.max()) if d.size else 0.0,
                  mean_out=float(d.mean()) if d.size else 0.0,
-                 max_lse=float(dl.max()) if dl.size else 0.0, rows=int(len(ref_l)))
+                 max_lse=float(dl.max()) if dl.size else 0.0, rows=int(len(ref_l)),
+                 max_rel=rel_max, mean_rel=rel_mean)
     say(f"  {what}: {stats}")
+    rr = row_rel_errors(got_o, ref_o) if d.size else np.zeros(0)
     worst = np.argsort(-d.max(axis=1))[:4] if d.size else []
     for r in worst:
         lab = tuple(rows[r]) if rows is not None else r
-        say(f"    row {lab}: max|d out|={d[r].max():.3e} |d lse|="
+        say(f"    row {lab}: max|d out|={d[r].max():.3e} rel={rr[r]:.3e} |d lse|="
             f"{abs(got_l[r] - ref_l[r]):.3e} lse={ref_l[r]:.4f}")
     assert not np.isnan(got_o).any(), f"{what}: NaN in output"
     assert stats["max_out"] <= tol["max_out"], f"{what}: max |d out| {stats['max_out']}"
     assert stats["mean_out"] <= tol["mean_out"], f"{what}: mean |d out| {stats['mean_out']}"
     assert stats["max_lse"] <= tol["lse"], f"{what}: max |d lse| {stats['max_lse']}"
+    assert rel_ok, f"{what}: per-row relative error max {rel_max:.3e} mean {rel_mean:.3e}"
     return stats
 
 

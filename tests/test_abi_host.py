@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert cakv.abi_version() == 1
+    assert cakv.abi_version() == 2
     for code, name in enumerate(["CAKV_OK", "CAKV_ERR_NULL", "CAKV_ERR_SHAPE", "CAKV_ERR_DTYPE",
                                  "CAKV_ERR_ALIGN", "CAKV_ERR_RANGE", "CAKV_ERR_HIP",
                                  "CAKV_ERR_INTERNAL"]):

@@ -17,7 +17,8 @@ import torch
 import cakv_synth as syn
 import context_attention_kv_amd as cakv
 import oracle
-from gpu_util import Inputs, all_rows, compare, gather_rows, run_forward, say, to_dev
+from gpu_util import (Inputs, all_rows, compare, expected_tiles, gather_rows, run_forward, say,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +94,7 @@ def test_per_block_ring_equals_oracle_and_state(dtype, Hq, Hkv, D):
         # fused call agrees with the chain of single steps
         fo, fl, ftc = run_forward(inp, r, counters=True)
         assert torch.equal(ftc, tc)
+        assert tc.cpu().tolist() == list(expected_tiles(w, r))
         tol = 1e-5 if dtype == "f32" else 2e-3
         assert (fo - out).abs().max().item() <= tol
 
@@ -251,7 +253,11 @@ def test_skip_block_leaves_state_untouched():
                            tile_counters=tc)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(before, (m, l, o)))
-    assert int(tc.sum()) == 0
+    # nothing computed; every tile of the block's grid counted as skipped
+    _, _, tiles = oracle.classify(w.C, 0, [2 * w.C], [w.C], causal=True, B=w.B, Hq=w.Hq,
+                                  tile_q=cakv.CAKV_TILE_Q, tile_k=cakv.CAKV_TILE_K)
+    assert tiles[0] == tiles[1] == 0 and tiles[2] > 0
+    assert tc.cpu().tolist() == list(tiles)
 
 
 def test_empty_problems_are_noops():

@@ -77,7 +77,8 @@ def test_decode_d64_bidirectional_bf16_out():
     rows = all_rows(w.B, w.Hq, w.Tn)
     ro, rl = oracle.attention(q, k, v, q_off=w.hist, k_off=0, causal=False, rows=rows)
     go, gl = gather_rows(out, lse, rows)
-    compare(go, gl, ro, rl, "bf16", "decode d=64 bidirectional, bf16 out", rows)
+    compare(go, gl, ro, rl, "bf16", "decode d=64 bidirectional, bf16 out", rows,
+            out_bf16=True)
 
 
 def test_decode_shuffled_gapped_empty_portions():

@@ -8,8 +8,8 @@ tokens across four GPUs", "A better mental model: move blocks past the
 queries", "Causal attention gives us another optimization"). At full size
 the oracle checks a seeded row sample (always including rows 0, 1, 127, 128,
 255, 256, C/2, C-2, C-1); smaller variants are checked on every row. The
-schedule is checked bit-exactly: the tiles the kernel computed, full and
-masked, must equal the oracle's brute-force pair count.
+schedule is checked bit-exactly: the tiles the kernel computed (full,
+masked) and skipped must equal the oracle's brute-force classification.
 """
 import numpy as np
 import pytest
@@ -32,7 +32,8 @@ def _check_rank(inp, rank, rows, tag):
     stats = compare(got_o, got_l, ref_o, ref_l, w.dtype, f"{tag} rank {rank}", rows)
     exp = expected_tiles(w, rank)
     got = tc.cpu().numpy()
-    assert got[0] == exp[0] and got[1] == exp[1], f"tiles {got[:2]} != oracle {exp[:2]}"
+    say(f"[{tag}] rank {rank}: tiles gpu {got.tolist()} oracle {list(exp)}")
+    assert got.tolist() == list(exp), f"tiles (full, masked, skipped) {got} != oracle {exp}"
     assert torch.isfinite(lse).all() or not w.causal
     return stats
 
@@ -80,7 +81,7 @@ def test_cfg4_full_size_sampled():
     say("[cfg4] generating inputs")
     inp = Inputs(w)
     rows = syn.sample_rows(w, per_head=12, seed=4)
-    keep = np.isin(rows[:, 0], [0, 7]) & np.isin(rows[:, 1], [0, 21, 42, 63])
+    keep = np.isin(rows[:, 1], np.arange(0, 64, 9))   # every batch row, 8 heads spread out
     _check_rank(inp, 3, rows[keep], "cfg4")
 
 
@@ -88,9 +89,8 @@ def test_cfg5_full_size_sampled():
     w = syn.WORKLOADS[5]
     say("[cfg5] generating inputs")
     inp = Inputs(w)
-    rows = syn.sample_rows(w, per_head=12, seed=5)
-    keep = np.isin(rows[:, 1], [0, 5, 31])
-    _check_rank(inp, 7, rows[keep], "cfg5")
+    rows = syn.sample_rows(w, per_head=12, seed=5)   # every one of the 32 query heads
+    _check_rank(inp, 7, rows, "cfg5")
 
 
 @pytest.mark.parametrize("case", [
