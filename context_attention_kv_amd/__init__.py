@@ -20,6 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcakv.so")
 
 CAKV_OK = 0
+CAKV_ERR_NULL, CAKV_ERR_SHAPE, CAKV_ERR_DTYPE, CAKV_ERR_ALIGN, CAKV_ERR_RANGE, CAKV_ERR_HIP = 1, 2, 3, 4, 5, 6
 CAKV_F32, CAKV_BF16 = 0, 1
 CAKV_FULL, CAKV_DIAG, CAKV_SKIP = 0, 1, 2
 CAKV_MAX_CHUNKS = 64
@@ -31,8 +32,9 @@ EXPORTED = (
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
     "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
     "cakv_decode_workspace_size", "cakv_forward_blocks", "cakv_backward_blocks",
-    "cakv_backward_workspace_size",
+    "cakv_backward_workspace_size", "cakv_decode_noalloc",
 )
+CAKV_DECODE_SCRATCH_BYTES = 32 << 20   # scratch array behind cakv_decode_noalloc
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
 
 
@@ -74,6 +76,7 @@ def _load_lib():
                                   P, I64, P], I),
         "cakv_backward_workspace_size": ([I, I, I, P], I),
         "cakv_decode_workspace_size": ([I, I, I, I, I, P, I, P], I),
+        "cakv_decode_noalloc": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -276,6 +279,34 @@ def cakv_decode(q, k_portions: Sequence, v_portions: Sequence, kv_offsets: Seque
                             D, int(q_offset), int(causal), float(scale), _ptr(out),
                             _dtype_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                             _stream(stream)), "cakv_decode")
+
+
+def cakv_decode_noalloc(q, k_portions: Sequence, v_portions: Sequence,
+                        kv_offsets: Sequence[int], q_offset: int, causal: bool, out, lse=None,
+                        scale: float = 0.0, stream=None):
+    """cakv_decode with the splits' states in the library's fixed per-GPU
+    scratch array (CAKV_DECODE_SCRATCH_BYTES) instead of a workspace: no device
+    memory is allocated, here or in the library. Calls that overlap on one GPU
+    share that array and must be ordered by the caller."""
+    _contig(q, out, lse, *k_portions, *v_portions)
+    B, Tn, Hq, D = q.shape
+    n = len(k_portions)
+    if len(v_portions) != n or len(kv_offsets) != n or n == 0:
+        raise ValueError("need the same positive number of K portions, V portions and offsets")
+    Hkv = k_portions[0].shape[2]
+    lens = []
+    for kp, vp in zip(k_portions, v_portions):
+        if kp.shape != vp.shape or kp.shape[0] != B or kp.shape[2] != Hkv or kp.shape[3] != D:
+            raise ValueError("every portion must be [B, L_j, Hkv, D] for K and V alike")
+        lens.append(int(kp.shape[1]))
+    karr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in k_portions])
+    varr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in v_portions])
+    larr = (ctypes.c_int64 * n)(*lens)
+    oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
+    _check(_lib.cakv_decode_noalloc(_ptr(q), karr, varr, larr, oarr, n, _dtype_code(q), B, Hq,
+                                    Hkv, Tn, D, int(q_offset), int(causal), float(scale),
+                                    _ptr(out), _dtype_code(out), _ptr(lse), _stream(stream)),
+           "cakv_decode_noalloc")
 
 
 def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: Sequence[int],

@@ -505,32 +505,54 @@ cakv_status cakv_decode_workspace_size(int B, int Hq, int Hkv, int Tn, int D,
     return ok();
 }
 
-cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
-                        const void* const* v_portions_host, const int64_t* kv_len_host,
-                        const int64_t* kv_off_host, int n_portions, int dtype, int B, int Hq,
-                        int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
-                        int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of cakv_decode shared with cakv_decode_noalloc (everything but the
+// workspace); fills the plan. `*empty` is set when there is nothing to do.
+cakv_status decode_check(const void* q, const void* const* k_portions_host,
+                         const void* const* v_portions_host, const int64_t* kv_len_host,
+                         const int64_t* kv_off_host, int n_portions, int dtype, int B, int Hq,
+                         int Hkv, int Tn, int D, void* out, int out_dtype, DecodePlan* p,
+                         bool* empty) {
+    *empty = false;
     if (dtype != CAKV_BF16 && dtype != CAKV_F32)
         return fail(CAKV_ERR_DTYPE, "dtype %d is neither CAKV_F32 nor CAKV_BF16", dtype);
     if (dtype != CAKV_BF16)
         return fail(CAKV_ERR_DTYPE, "cakv_decode takes bf16 inputs only");
     if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
         return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
-    DecodePlan p;
-    cakv_status s = decode_plan(B, Hq, Hkv, Tn, D, kv_len_host, n_portions, &p);
+    cakv_status s = decode_plan(B, Hq, Hkv, Tn, D, kv_len_host, n_portions, p);
     if (s != CAKV_OK) return s;
-    if (B == 0 || Tn == 0) return ok();
+    if (B == 0 || Tn == 0) {
+        *empty = true;
+        return ok();
+    }
     if (!q || !out) return fail(CAKV_ERR_NULL, "q or out is NULL");
     if (!k_portions_host || !v_portions_host || !kv_off_host)
         return fail(CAKV_ERR_NULL, "portion pointer / offset array is NULL");
-    if (!workspace) return fail(CAKV_ERR_NULL, "workspace is NULL");
-    if (workspace_bytes < p.ws_bytes)
-        return fail(CAKV_ERR_SHAPE, "workspace of %lld bytes, %lld needed",
-                    (long long)workspace_bytes, p.ws_bytes);
-    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
-        return fail(CAKV_ERR_ALIGN, "q/out/workspace not 16-byte aligned");
+    if (!aligned16(q) || !aligned16(out)) return fail(CAKV_ERR_ALIGN, "q/out not 16-byte aligned");
+    for (int j = 0; j < n_portions; ++j) {
+        if (kv_len_host[j] == 0) continue;
+        const void* kp = k_portions_host[j];
+        const void* vp = v_portions_host[j];
+        if (!kp || !vp) return fail(CAKV_ERR_NULL, "portion %d pointer is NULL", j);
+        if (!aligned16(kp) || !aligned16(vp))
+            return fail(CAKV_ERR_ALIGN, "portion %d not 16-byte aligned", j);
+    }
+    return ok();
+}
 
+// The two decode kernels on a checked problem, with the splits' states in
+// `workspace` (at least plan.ws_bytes, 16-byte aligned).
+cakv_status decode_launch(const void* q, const void* const* k_portions_host,
+                          const void* const* v_portions_host, const int64_t* kv_len_host,
+                          const int64_t* kv_off_host, int n_portions, int B, int Hq, int Hkv,
+                          int Tn, int D, int64_t q_off, int causal, float scale, void* out,
+                          int out_dtype, float* lse, const DecodePlan& p, void* workspace,
+                          void* stream) {
+    cakv_status s;
     cakv::DecArgs a;
     std::memset(&a, 0, sizeof a);
     int tile = 0;
@@ -539,13 +561,8 @@ cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
         a.kv_len[j] = (int)kv_len_host[j];
         a.kv_off[j] = kv_off_host[j];
         if (kv_len_host[j] > 0) {
-            const void* kp = k_portions_host[j];
-            const void* vp = v_portions_host[j];
-            if (!kp || !vp) return fail(CAKV_ERR_NULL, "portion %d pointer is NULL", j);
-            if (!aligned16(kp) || !aligned16(vp))
-                return fail(CAKV_ERR_ALIGN, "portion %d not 16-byte aligned", j);
-            a.k[j] = kp;
-            a.v[j] = vp;
+            a.k[j] = k_portions_host[j];
+            a.v[j] = v_portions_host[j];
         }
         tile += (int)((kv_len_host[j] + cakv::kDecTile - 1) / cakv::kDecTile);
     }
@@ -569,6 +586,54 @@ cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
     s = hip_status(cakv::launch_decode_split(a, D, stream), "decode split launch");
     if (s != CAKV_OK) return s;
     return hip_status(cakv::launch_decode_merge(a, D, stream), "decode merge launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
+                        const void* const* v_portions_host, const int64_t* kv_len_host,
+                        const int64_t* kv_off_host, int n_portions, int dtype, int B, int Hq,
+                        int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
+                        int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+    DecodePlan p;
+    bool empty = false;
+    cakv_status s = decode_check(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
+                                 n_portions, dtype, B, Hq, Hkv, Tn, D, out, out_dtype, &p, &empty);
+    if (s != CAKV_OK || empty) return s;
+    if (!workspace) return fail(CAKV_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < p.ws_bytes)
+        return fail(CAKV_ERR_SHAPE, "workspace of %lld bytes, %lld needed",
+                    (long long)workspace_bytes, p.ws_bytes);
+    if (!aligned16(workspace)) return fail(CAKV_ERR_ALIGN, "workspace not 16-byte aligned");
+    return decode_launch(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
+                         n_portions, B, Hq, Hkv, Tn, D, q_off, causal, scale, out, out_dtype, lse,
+                         p, workspace, stream);
+}
+
+cakv_status cakv_decode_noalloc(const void* q, const void* const* k_portions_host,
+                                const void* const* v_portions_host, const int64_t* kv_len_host,
+                                const int64_t* kv_off_host, int n_portions, int dtype, int B,
+                                int Hq, int Hkv, int Tn, int D, int64_t q_off, int causal,
+                                float scale, void* out, int out_dtype, float* lse, void* stream) {
+    DecodePlan p;
+    bool empty = false;
+    cakv_status s = decode_check(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
+                                 n_portions, dtype, B, Hq, Hkv, Tn, D, out, out_dtype, &p, &empty);
+    if (s != CAKV_OK || empty) return s;
+    if (p.ws_bytes > (long long)CAKV_DECODE_SCRATCH_BYTES)
+        return fail(CAKV_ERR_SHAPE,
+                    "cakv_decode_noalloc: these sizes need %lld bytes of split state, above the "
+                    "library's fixed %lld-byte scratch; use cakv_decode with a workspace",
+                    p.ws_bytes, (long long)CAKV_DECODE_SCRATCH_BYTES);
+    void* ws = nullptr;
+    s = hip_status(cakv::decode_scratch_address(&ws), "decode scratch address");
+    if (s != CAKV_OK) return s;
+    return decode_launch(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
+                         n_portions, B, Hq, Hkv, Tn, D, q_off, causal, scale, out, out_dtype, lse,
+                         p, ws, stream);
 }
 
 cakv_status cakv_diag_mfma_burn(int zero_operands, int64_t iters, float* sink, void* stream) {

@@ -40,6 +40,11 @@ struct DecArgs {
     float* lse;                             // [B, Hq, Tn] or null
 };
 
+// Device address of this device's decode scratch array
+// (CAKV_DECODE_SCRATCH_BYTES); resolved on the first call on each device
+// (the device current at the call), then cached. Returns a hipError_t as int.
+int decode_scratch_address(void** ptr);
+
 int launch_decode_split(const DecArgs& a, int D, void* stream);
 int launch_decode_merge(const DecArgs& a, int D, void* stream);
 

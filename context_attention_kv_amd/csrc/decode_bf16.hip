@@ -26,9 +26,40 @@
 // L = sum_s 2^(m_s-M) l_s, out = sum_s 2^(m_s-M) o_s / L, lse = (M + log2 L) ln 2.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "decode_args.h"
 
+// Scratch of the allocation-free decode entry point (cakv_decode_noalloc):
+// the splits' (m, l, o) states live here instead of in a caller workspace.
+// One copy per GPU, held until the process ends. Host code never passes this
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, resolved once per device by decode_scratch_address below.
+static __device__ __align__(256) char scratch[CAKV_DECODE_SCRATCH_BYTES];
+
 namespace cakv {
+
+int decode_scratch_address(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

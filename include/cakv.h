@@ -70,6 +70,8 @@ extern "C" {
 #define CAKV_MAX_CHUNKS 64 /* most key/value blocks one forward call takes */
 #define CAKV_TILE_Q 32     /* query rows per counted tile */
 #define CAKV_TILE_K 64     /* keys per counted tile */
+/* bytes of the per-GPU scratch array behind cakv_decode_noalloc (32 MiB) */
+#define CAKV_DECODE_SCRATCH_BYTES (32LL << 20)
 
 typedef enum {
     CAKV_OK = 0,
@@ -323,6 +325,28 @@ cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
                         int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
                         int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
                         void* stream);
+
+/*
+ * cakv_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code recorded under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The splits' states go to a scratch array
+ * of CAKV_DECODE_SCRATCH_BYTES that the library holds in device memory, one
+ * per GPU, for the life of the process; the call itself allocates and frees
+ * nothing (its first call on a GPU looks up that GPU's array address). All
+ * arguments, results and errors are those of cakv_decode, plus
+ * CAKV_ERR_SHAPE, before anything is launched, when the sizes need more
+ * split state than the array holds (cakv_decode_workspace_size > 32 MiB;
+ * the million-token history with up to 16 new tokens needs ~25.6 MB).
+ * Nothing in the array needs clearing: every entry a call reads was written
+ * earlier in the same call. Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams, or threads)
+ * race and must be ordered by the caller.
+ */
+cakv_status cakv_decode_noalloc(const void* q, const void* const* k_portions_host,
+                                const void* const* v_portions_host, const int64_t* kv_len_host,
+                                const int64_t* kv_off_host, int n_portions, int dtype, int B,
+                                int Hq, int Hkv, int Tn, int D, int64_t q_off, int causal,
+                                float scale, void* out, int out_dtype, float* lse, void* stream);
 
 /*
  * Bytes of workspace cakv_decode needs for these sizes (written to the HOST

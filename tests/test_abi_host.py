@@ -236,6 +236,41 @@ def test_decode_errors_and_workspace_size():
     assert dec(B=0, q=None, out=None, ws=None) == 0   # nothing to do
 
 
+def test_decode_noalloc_errors_and_scratch_limit():
+    """cakv_decode_noalloc checks exactly what cakv_decode checks (no
+    workspace argument), and rejects sizes whose split state exceeds its
+    fixed scratch array before touching the device."""
+    I64 = ctypes.c_int64
+    lens = (I64 * 3)(1000, 0, 64)
+    offs = (I64 * 3)(0, 1000, 1000)
+    ptrs = (ctypes.c_void_p * 3)(FAKE, None, FAKE)
+
+    def dec(q=FAKE, k=ptrs, v=ptrs, n=3, dtype=1, B=1, Hq=8, Hkv=2, Tn=4, D=128, out=FAKE,
+            odt=0):
+        return L.cakv_decode_noalloc(q, k, v, lens, offs, n, dtype, B, Hq, Hkv, Tn, D, 1004, 1,
+                                     0.0, out, odt, None, None)
+    assert dec(dtype=0) == 3
+    assert dec(odt=5) == 3
+    assert dec(n=0) == 5
+    assert dec(D=80) == 2
+    assert dec(Hq=8, Hkv=3) == 2
+    assert dec(q=None) == 1
+    assert dec(out=MIS) == 4
+    assert dec(k=None) == 1
+    assert dec(B=0, q=None, out=None) == 0   # nothing to do
+    nb = I64(0)
+    assert L.cakv_decode_workspace_size(64, 32, 8, 16, 128, lens, 3, ctypes.byref(nb)) == 0
+    assert nb.value > cakv.CAKV_DECODE_SCRATCH_BYTES
+    assert dec(B=64, Hq=32, Hkv=8, Tn=16) == 2
+    assert "scratch" in L.cakv_last_error().decode()
+    # the million-token history (32 query heads on 8, one to sixteen new
+    # tokens) fits
+    big = (I64 * 8)(*([131072] * 7 + [131073]))
+    for tn in (1, 16):
+        assert L.cakv_decode_workspace_size(1, 32, 8, tn, 128, big, 8, ctypes.byref(nb)) == 0
+        assert nb.value <= cakv.CAKV_DECODE_SCRATCH_BYTES
+
+
 def test_forward_blocks_errors():
     I64 = ctypes.c_int64
     lens = (I64 * 2)(100, 0)
