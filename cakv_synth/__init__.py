@@ -25,7 +25,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB_PATH = os.path.join(_HERE, "libcakvsynth.so")
+# CAKV_SYNTH_LIB selects another build of synth.c (the host-sanitizer test
+# build, tests/sanitize/run_host_sanitizers.py)
+_LIB_PATH = os.environ.get("CAKV_SYNTH_LIB") or os.path.join(_HERE, "libcakvsynth.so")
 _lib = None
 
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2

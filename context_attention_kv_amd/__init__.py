@@ -17,7 +17,10 @@ import os
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcakv.so")
+# CAKV_LIB_PATH selects another build of the same library: the host-only
+# sanitizer build of the C ABI layer, whose launchers all return an error
+# (tests/sanitize/run_host_sanitizers.py)
+LIB_PATH = os.environ.get("CAKV_LIB_PATH") or os.path.join(_HERE, "libcakv.so")
 
 CAKV_OK = 0
 CAKV_ERR_NULL, CAKV_ERR_SHAPE, CAKV_ERR_DTYPE, CAKV_ERR_ALIGN, CAKV_ERR_RANGE, CAKV_ERR_HIP = 1, 2, 3, 4, 5, 6

@@ -35,7 +35,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# CAKV_ORACLE_LIB selects another build of oracle.c (the host-sanitizer test
+# build, tests/sanitize/run_host_sanitizers.py)
+_LIB_PATH = os.environ.get("CAKV_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
