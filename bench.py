@@ -544,6 +544,11 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
+    # caller-owned workspace of the key-split path for small shares (none
+    # when the share fills the GPU)
+    ws_bytes = cakv.cakv_forward_workspace_size(cakv.CAKV_BF16 if w.dtype == "bf16" else cakv.CAKV_F32,
+                                                w.B, w.Hq, w.Hkv, C, w.D)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda") if ws_bytes else None
     stream = torch.cuda.current_stream()
     n_launch = len(ranks)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * n_launch)]
@@ -553,7 +558,7 @@ def main():
         for i, r in enumerate(ranks):
             if timed_idx is not None:
                 starts[timed_idx * n_launch + i].record(stream)
-            cakv.cakv_local_shard_forward(qd[r], kb, vb, r, w.causal, out[r], lse[r])
+            cakv.cakv_local_shard_forward(qd[r], kb, vb, r, w.causal, out[r], lse[r], workspace=ws)
             if timed_idx is not None:
                 ends[timed_idx * n_launch + i].record(stream)
 
@@ -586,7 +591,8 @@ def main():
     traffic = traffic_for(w.name)
     roofline = {
         "bound": "mfma" if is_bf16 else "alu",
-        "kernel": forward_kernel_name(w),
+        "kernel": forward_kernel_name(w) + (" + split_merge_kernel (key split)" if ws is not None
+                                            else ""),
         "achieved": round(achieved, 2),
         "peak": round(peak, 1),
         "unit": "TFLOP/s",

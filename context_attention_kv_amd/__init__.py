@@ -35,7 +35,7 @@ EXPORTED = (
     "cakv_schedule", "cakv_state_init", "cakv_block_update", "cakv_finalize",
     "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
     "cakv_decode_workspace_size", "cakv_forward_blocks", "cakv_backward_blocks",
-    "cakv_backward_workspace_size", "cakv_decode_noalloc",
+    "cakv_backward_workspace_size", "cakv_decode_noalloc", "cakv_forward_workspace_size",
 )
 CAKV_DECODE_SCRATCH_BYTES = 32 << 20   # scratch array behind cakv_decode_noalloc
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
@@ -71,10 +71,13 @@ def _load_lib():
         "cakv_block_update": ([P, P, P, I, I, I, I, I, I, I, I64, I64, I, F, P, P, P, P, P], I),
         "cakv_finalize": ([P, P, P, P, I, P, I, I, I, I, P], I),
         "cakv_lse_merge": ([P, P, P, P, P, P, I, I, I, I, P], I),
-        "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, P], I),
+        "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, I64, P, P],
+                                     I),
         "cakv_diag_mfma_burn": ([I, I64, P, P], I),
         "cakv_decode": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P], I),
-        "cakv_forward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, P], I),
+        "cakv_forward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P,
+                                 P], I),
+        "cakv_forward_workspace_size": ([I, I, I, I, I, I, P], I),
         "cakv_backward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, P, P, P, P, P,
                                   P, I64, P], I),
         "cakv_backward_workspace_size": ([I, I, I, P], I),
@@ -206,11 +209,41 @@ def cakv_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, stream=None):
                                _ptr(lse_out), B, Hq, Tq, D, _stream(stream)), "cakv_lse_merge")
 
 
+def cakv_forward_workspace_size(dtype_code: int, B: int, Hq: int, Hkv: int, Tq: int,
+                                D: int) -> int:
+    """Bytes of workspace that lets the whole-shard forward split a small
+    share's key range (0 when it is not split)."""
+    out = ctypes.c_int64(0)
+    _check(_lib.cakv_forward_workspace_size(dtype_code, B, Hq, Hkv, Tq, D, ctypes.byref(out)),
+           "cakv_forward_workspace_size")
+    return out.value
+
+
+def _fwd_workspace(workspace, q, Hkv: int, Tq: int):
+    """(pointer, bytes, tensor) of the forward workspace: "auto" allocates
+    what cakv_forward_workspace_size asks for (nothing when it is 0), None
+    passes none, a tensor is passed as given."""
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        B, _, Hq, D = q.shape
+        nbytes = cakv_forward_workspace_size(_dtype_code(q), B, Hq, Hkv, Tq, D)
+        if nbytes == 0:
+            return None, 0, None
+        import torch
+        workspace = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=q.device)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
 def cakv_local_shard_forward(q_local, k_blocks: Sequence, v_blocks: Sequence, rank: int,
                              causal: bool, out, lse=None, scale: float = 0.0,
-                             tile_counters=None, stream=None):
+                             tile_counters=None, workspace="auto", stream=None):
     """One rank's share: q_local [B, C, Hq, D] against N blocks [B, C, Hkv, D]
-    in ring order rank, rank-1, ...; writes out [B, C, Hq, D] and lse [B, Hq, C]."""
+    in ring order rank, rank-1, ...; writes out [B, C, Hq, D] and lse [B, Hq, C].
+    workspace: "auto" (allocate cakv_forward_workspace_size bytes when a small
+    share can use them), None, or a device tensor."""
     _contig(q_local, out, lse, *k_blocks, *v_blocks)
     B, C, Hq, D = q_local.shape
     n = len(k_blocks)
@@ -222,9 +255,10 @@ def cakv_local_shard_forward(q_local, k_blocks: Sequence, v_blocks: Sequence, ra
             raise ValueError("every block must be [B, C, Hkv, D] with the query dtype")
     karr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_blocks])
     varr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_blocks])
+    wp, wb, _keep = _fwd_workspace(workspace, q_local, Hkv, C)
     _check(_lib.cakv_local_shard_forward(_ptr(q_local), karr, varr, _dtype_code(q_local), B,
                                          Hq, Hkv, C, n, D, rank, int(causal), float(scale),
-                                         _ptr(out), _dtype_code(out), _ptr(lse),
+                                         _ptr(out), _dtype_code(out), _ptr(lse), wp, wb,
                                          _counters(tile_counters), _stream(stream)),
            "cakv_local_shard_forward")
 
@@ -314,7 +348,7 @@ def cakv_decode_noalloc(q, k_portions: Sequence, v_portions: Sequence,
 
 def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: Sequence[int],
                         q_offset: int, causal: bool, out, lse=None, scale: float = 0.0,
-                        tile_counters=None, stream=None):
+                        tile_counters=None, workspace="auto", stream=None):
     """Queries q [B, Tq, Hq, D] at positions q_offset ... against blocks
     [B, L_t, Hkv, D] of any lengths at global offsets kv_offsets[t], in the
     order given; writes out [B, Tq, Hq, D] and lse [B, Hq, Tq]."""
@@ -334,10 +368,12 @@ def cakv_forward_blocks(q, k_blocks: Sequence, v_blocks: Sequence, kv_offsets: S
     varr = (ctypes.c_void_p * n)(*[t.data_ptr() if t.numel() else None for t in v_blocks])
     larr = (ctypes.c_int64 * n)(*lens)
     oarr = (ctypes.c_int64 * n)(*[int(x) for x in kv_offsets])
+    wp, wb, _keep = _fwd_workspace(workspace, q, Hkv, Tq)
     _check(_lib.cakv_forward_blocks(_ptr(q), karr, varr, larr, oarr, n, _dtype_code(q), B, Hq,
                                     Hkv, Tq, D, int(q_offset), int(causal), float(scale),
-                                    _ptr(out), _dtype_code(out), _ptr(lse), _counters(tile_counters),
-                                    _stream(stream)), "cakv_forward_blocks")
+                                    _ptr(out), _dtype_code(out), _ptr(lse), wp, wb,
+                                    _counters(tile_counters), _stream(stream)),
+           "cakv_forward_blocks")
 
 
 def cakv_backward_workspace_size(B: int, Hq: int, Tq: int) -> int:

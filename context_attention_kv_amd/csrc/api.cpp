@@ -90,7 +90,49 @@ cakv_status set_grid(cakv::FwdArgs& a, int dtype, int D) {
     if (n_wg > 2147483647LL) return fail(CAKV_ERR_SHAPE, "forward grid too large (%lld workgroups)", n_wg);
     a.wg_per_bg = (int)per_bg;
     a.n_wg = (int)n_wg;
+    a.n_split = 1;
     return CAKV_OK;
+}
+
+// Key splits and workspace bytes of the split path for a whole-shard forward
+// (bf16 four-wave shapes whose grid leaves resident slots empty); 1 / 0 when
+// the grid is not split.
+struct SplitPlan {
+    int n_split;
+    long long rows;
+    long long bytes;
+};
+SplitPlan split_plan(int dtype, int B, int Hq, int Hkv, int Tq, int D) {
+    SplitPlan p{1, (long long)B * Hq * Tq, 0};
+    if (dtype != CAKV_BF16 || p.rows == 0) return p;
+    const long long G = Hq / Hkv;
+    const long long nw = cakv::fwd_bf16_waves(D, (int)G);
+    if (nw != 4) return p;   // only the four-wave kernel splits
+    const long long per_bg = (G * ((Tq + 31LL) / 32) + nw - 1) / nw;
+    const long long n_wg = (long long)B * Hkv * per_bg;
+    // enough parts that the grid fills the resident workgroup slots of the
+    // four-wave kernel (256 CUs x 2 workgroups at d = 128, x 4 at d = 64, as
+    // its registers and LDS allow), at most 8
+    const long long slots = 256LL * (D == 64 ? 4 : 2);
+    if (n_wg >= slots) return p;
+    const int S = (int)std::min(8LL, (slots + n_wg - 1) / n_wg);
+    if (S <= 1) return p;
+    p.n_split = S;
+    const long long ml = 2LL * S * p.rows;
+    p.bytes = ((ml + 3) / 4 * 4 + (long long)S * p.rows * D) * 4;
+    return p;
+}
+
+// Use the split path when the caller's workspace holds it.
+void apply_split(cakv::FwdArgs& a, const SplitPlan& p, void* workspace, int64_t workspace_bytes) {
+    if (p.n_split <= 1 || !workspace || workspace_bytes < p.bytes) return;
+    float* w = static_cast<float*>(workspace);
+    const long long ml = 2LL * p.n_split * p.rows;
+    a.n_split = p.n_split;
+    a.split_rows = p.rows;
+    a.split_m = w;
+    a.split_l = w + (long long)p.n_split * p.rows;
+    a.split_o = w + (ml + 3) / 4 * 4;
 }
 
 int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
@@ -285,7 +327,8 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
                                      const void* const* v_blocks_host, int dtype, int B,
                                      int Hq, int Hkv, int chunk_len, int n_chunks, int D,
                                      int rank, int causal, float scale, void* out,
-                                     int out_dtype, float* lse, int64_t* tile_counters,
+                                     int out_dtype, float* lse, void* workspace,
+                                     int64_t workspace_bytes, int64_t* tile_counters,
                                      void* stream) {
     cakv_status s = check_common(dtype, B, Hq, Hkv, chunk_len, chunk_len, D);
     if (s != CAKV_OK) return s;
@@ -300,6 +343,8 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     if (!k_blocks_host || !v_blocks_host) return fail(CAKV_ERR_NULL, "block pointer array is NULL");
     if (!aligned16(q_local) || !aligned16(out))
         return fail(CAKV_ERR_ALIGN, "q_local/out not 16-byte aligned");
+    if (workspace && !aligned16(workspace)) return fail(CAKV_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (workspace_bytes < 0) return fail(CAKV_ERR_SHAPE, "negative workspace size");
     if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
         return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
 
@@ -342,6 +387,7 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     s = set_grid(a, dtype, D);
     if (s != CAKV_OK) return s;
+    apply_split(a, split_plan(dtype, B, Hq, Hkv, chunk_len, D), workspace, workspace_bytes);
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
 }
 
@@ -350,6 +396,7 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
                                 const int64_t* kv_off_host, int n_blocks, int dtype, int B,
                                 int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
                                 float scale, void* out, int out_dtype, float* lse,
+                                void* workspace, int64_t workspace_bytes,
                                 int64_t* tile_counters, void* stream) {
     cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
     if (s != CAKV_OK) return s;
@@ -366,6 +413,8 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     if (!q || !out) return fail(CAKV_ERR_NULL, "q or out is NULL");
     if (!k_blocks_host || !v_blocks_host) return fail(CAKV_ERR_NULL, "block pointer array is NULL");
     if (!aligned16(q) || !aligned16(out)) return fail(CAKV_ERR_ALIGN, "q/out not 16-byte aligned");
+    if (workspace && !aligned16(workspace)) return fail(CAKV_ERR_ALIGN, "workspace not 16-byte aligned");
+    if (workspace_bytes < 0) return fail(CAKV_ERR_SHAPE, "negative workspace size");
     if (tile_counters && (reinterpret_cast<uintptr_t>(tile_counters) & 7u))
         return fail(CAKV_ERR_ALIGN, "tile_counters not 8-byte aligned");
 
@@ -400,7 +449,17 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     s = set_grid(a, dtype, D);
     if (s != CAKV_OK) return s;
+    apply_split(a, split_plan(dtype, B, Hq, Hkv, Tq, D), workspace, workspace_bytes);
     return hip_status(launch_fwd(a, dtype, D, stream), "forward_blocks launch");
+}
+
+cakv_status cakv_forward_workspace_size(int dtype, int B, int Hq, int Hkv, int Tq, int D,
+                                        int64_t* bytes_host) {
+    if (!bytes_host) return fail(CAKV_ERR_NULL, "bytes_host is NULL");
+    const cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
+    if (s != CAKV_OK) return s;
+    *bytes_host = split_plan(dtype, B, Hq, Hkv, Tq, D).bytes;
+    return ok();
 }
 
 cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host) {

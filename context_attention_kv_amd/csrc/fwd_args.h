@@ -34,7 +34,15 @@ struct FwdArgs {
     long long skip_tiles;                 // CAKV_TILE_K-key tiles of blocks dropped from the
                                           // list as SKIP, per 32-row tile (counters only)
     int wg_per_bg;                        // workgroups per (batch, kv head)
-    int n_wg;                             // total workgroups
+    int n_wg;                             // total workgroups (per key split)
+    // key splits of a small grid (bf16 four-wave kernel, whole-shard calls):
+    // n_split workgroups per query tile write partial states here, and a
+    // merge kernel finalises them into out / lse; n_split = 1: no split
+    int n_split;
+    long long split_rows;                 // B * Hq * Tq
+    float* split_m;                       // [n_split, rows] max, log2 units
+    float* split_l;                       // [n_split, rows]
+    float* split_o;                       // [n_split, rows, D] unnormalised
 };
 
 // Launchers (return the hipError_t of the launch as int).

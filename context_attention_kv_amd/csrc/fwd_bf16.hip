@@ -220,6 +220,21 @@ __device__ __forceinline__ void cursor_next(const FwdArgs& a, const HeadAt& at, 
     }
 }
 
+// Move cursor c forward by n tiles of its sequence.
+__device__ __forceinline__ void cursor_skip(const FwdArgs& a, const HeadAt& at, Cursor& c, int n) {
+    while (n > 0 && c.need > 0) {
+        const int left = (c.need + kBK - 1) / kBK - c.ti;   // tiles left in block c.bi
+        if (n < left) {
+            c.ti += n;
+            return;
+        }
+        n -= left;
+        c.ti = 0;
+        ++c.bi;
+        cursor_load(a, at, c);
+    }
+}
+
 // Tiles (64 keys) that a workgroup whose tile sequence has T tiles never
 // visits: whole blocks after its last query (causal), the tails of blocks
 // past it, and the tiles of blocks the host's schedule left out of the list.
@@ -640,13 +655,20 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     const int l32 = lane & 31, hh = lane >> 5;
     const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;   // LDS address of the buffers
 
-    // ---- workgroup -> (batch, kv head, query tile); XCD-contiguous order ----
+    // ---- workgroup -> (batch, kv head, query tile, key split); XCD-contiguous order ----
+    // With S = a.n_split > 1 (small grids), S workgroups share a query tile,
+    // each folding one contiguous part of its tile sequence into a partial
+    // state that split_merge_kernel combines.
+    const int S = a.n_split;
     const int bid = blockIdx.x;
-    const int per = a.n_wg / 8, rem = a.n_wg % 8;
+    const int n_all = a.n_wg * S;
+    const int per = n_all / 8, rem = n_all % 8;
     const int xcd = bid % 8, idx = bid / 8;
     const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
-    const int bg = logical / a.wg_per_bg;
-    const int qt = a.wg_per_bg - 1 - (logical % a.wg_per_bg);  // heaviest first
+    const int sp = logical % S;
+    const int lwg = logical / S;
+    const int bg = lwg / a.wg_per_bg;
+    const int qt = a.wg_per_bg - 1 - (lwg % a.wg_per_bg);  // heaviest first
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.Hq / a.Hkv;
     const int npblk = (a.Tq + RW - 1) / RW;
@@ -723,9 +745,12 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
 
     // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
     const HeadAt at{b, g, kv_rs, D, wg_last_pos, wave_first_pos, a.causal};
-    int T = 0;
-    for (int t = 0; t < a.n_blocks; ++t) T += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
-    if constexpr (COUNT) n_skip = wave_valid ? skipped_unvisited(a, T) : 0u;
+    int T_all = 0;
+    for (int t = 0; t < a.n_blocks; ++t) T_all += (keys_needed(a, t, wg_last_pos) + kBK - 1) / kBK;
+    if constexpr (COUNT) n_skip = wave_valid && sp == 0 ? skipped_unvisited(a, T_all) : 0u;
+    // this workgroup's part of the sequence: tiles [t_lo, t_lo + T)
+    const int t_lo = (int)((long long)T_all * sp / S);
+    const int T = (int)((long long)T_all * (sp + 1) / S) - t_lo;
 
     // Tile copies: copy n of every wave fills 1 KB region 4n + wave of the K
     // and of the V tile.
@@ -739,6 +764,7 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
         cpv[n] = (unsigned)(2 * (row * kv_rs + 8 * (p ^ vswz<D>(row))));
     }
     Cursor ld = cursor_first(a, at);   // next tile to copy
+    cursor_skip(a, at, ld, t_lo);
     auto issue = [&](unsigned buf) {
         const int key0 = ld.ti * kBK;
         const int rows = min(kBK, ld.len - key0);
@@ -776,6 +802,7 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     constexpr int NQK = 2 * C::DSTEPS;   // Q K^T products per tile
 
     Cursor cq = cursor_first(a, at);   // tile this wave computes
+    cursor_skip(a, at, cq, t_lo);
     for (int t = 0; t < T; ++t) {
         const int buf = t & 1;
         // the other buffer was last read before the barrier that ended the
@@ -882,14 +909,32 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: store state, or finalise into out / lse ----
+    // ---- epilogue: store state, a split's partial state, or finalise into out / lse ----
     if (wave_valid) {
         const int row = row0 + l32;
         const float l_tot = half_sum(l_run);
         if (row < a.Tq) {
             const long long si = ((long long)b * a.Hq + h) * a.Tq + row;
             const long long oi = (((long long)b * a.Tq + row) * a.Hq + h) * D;
-            if (a.store_state) {
+            if (S > 1) {
+                // m in log2 units (-inf when the split saw no key of the row),
+                // l, and the unnormalised o of split sp
+                const long long wi = (long long)sp * a.split_rows + si;
+                if (hh == 0) {
+                    a.split_m[wi] = m_run;
+                    a.split_l[wi] = l_tot;
+                }
+                float* orow = a.split_o + wi * D;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        f32x4 x;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) x[jj] = o_acc[db][4 * ib + jj];
+                        *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * ib + 4 * hh) = x;
+                    }
+            } else if (a.store_state) {
                 if (hh == 0) {
                     a.m[si] = m_run * kLn2;
                     a.l[si] = l_tot;
@@ -939,14 +984,63 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
 // +43 %, small d = 128 shares +36 %, the B=8 H=64 T=32768 share +4 %).
 bool use_four_waves(int D, int G) { return D == 64 || G == 1; }
 
+// Combine the S partial states of each row (log-sum-exp rule in log2 units):
+// M = max_s m_s, L = sum_s 2^(m_s - M) l_s, out = sum_s 2^(m_s - M) o_s / L,
+// lse = (M + log2 L) ln 2; a row no split saw gives out = 0, lse = -inf.
+// D / 4 threads per row, 4 elements each.
+template <int D>
+__global__ void __launch_bounds__(256) split_merge_kernel(const FwdArgs a) {
+    constexpr int TPR = D / 4;
+    const long long rows = a.split_rows;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long si = i / TPR;
+    if (si >= rows) return;
+    const int c = (int)(i % TPR) * 4;
+    const int S = a.n_split;
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, a.split_m[sp * rows + si]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+    if (M > -INFINITY) {
+        for (int sp = 0; sp < S; ++sp) {
+            const long long wi = sp * rows + si;
+            const float w = fast_exp2(a.split_m[wi] - M);
+            L += w * a.split_l[wi];
+            const f32x4 x = *reinterpret_cast<const f32x4*>(a.split_o + wi * D + c);
+            o += w * x;
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    o *= inv;
+    // si = (b * Hq + h) * Tq + row
+    const long long row = si % a.Tq, bh = si / a.Tq;
+    const long long h = bh % a.Hq, b = bh / a.Hq;
+    const long long oi = ((b * a.Tq + row) * a.Hq + h) * D + c;
+    if (a.out_bf16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + oi) = __builtin_convertvector(o, bf16x4);
+    } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + oi) = o;
+    }
+    if (c == 0 && a.lse) a.lse[si] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
 template <int D>
 int launch(const FwdArgs& a, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (use_four_waves(D, a.Hq / a.Hkv)) {
+        const unsigned grid = (unsigned)((long long)a.n_wg * a.n_split);
         if (a.counters)
-            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, true>), dim3(a.n_wg), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, true>), dim3(grid), dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, false>), dim3(a.n_wg), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, false>), dim3(grid), dim3(256), 0, s, a);
+        if (a.n_split > 1) {
+            const int e = (int)hipGetLastError();
+            if (e) return e;
+            const long long threads = a.split_rows * (D / 4);
+            hipLaunchKernelGGL((split_merge_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
+                               dim3(256), 0, s, a);
+        }
     } else if (a.counters) {
         hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0, s, a);
     } else {

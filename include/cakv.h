@@ -210,8 +210,19 @@ cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_
  * k_blocks_host, v_blocks_host: HOST arrays of n_chunks device pointers,
  *   block j = [B, chunk_len, Hkv, D] holding positions [j*chunk_len, ...);
  * out: [B, chunk_len, Hq, D] in out_dtype; lse: [B, Hq, chunk_len] fp32
- *   (nullable); tile_counters: as for cakv_block_update, over the grids of
- *   all n_chunks blocks (nullable).
+ *   (nullable);
+ * workspace (nullable), workspace_bytes: device scratch owned by the caller,
+ *   16-byte aligned. When the share is too small to fill the GPU (few query
+ *   rows; bf16 with one query head per key/value head or d_k = 64) and the
+ *   workspace holds cakv_forward_workspace_size bytes, each query tile's key
+ *   range is cut into parts folded side by side, whose partial states are
+ *   combined by the log-sum-exp rule (page section "Training and inference
+ *   stress this dimension differently": partial results over key portions
+ *   combine). Otherwise, or with NULL, the running state stays on chip for
+ *   the whole ring. Both give the same result up to fp32 rounding order;
+ *   calls sharing a workspace must not overlap in time;
+ * tile_counters: as for cakv_block_update, over the grids of all n_chunks
+ *   blocks (nullable).
  * Errors: as above plus rank outside [0, n_chunks), n_chunks outside
  * [1, CAKV_MAX_CHUNKS], a NULL block pointer that the schedule would read.
  */
@@ -219,7 +230,8 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
                                      const void* const* v_blocks_host, int dtype, int B,
                                      int Hq, int Hkv, int chunk_len, int n_chunks, int D,
                                      int rank, int causal, float scale, void* out,
-                                     int out_dtype, float* lse, int64_t* tile_counters,
+                                     int out_dtype, float* lse, void* workspace,
+                                     int64_t workspace_bytes, int64_t* tile_counters,
                                      void* stream);
 
 /*
@@ -237,7 +249,8 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
  *   device pointers, block t = [B, kv_len_host[t], Hkv, D] with key 0 at
  *   global position kv_off_host[t] (HOST int64 arrays; an empty block's
  *   pointers may be NULL);
- * out, lse, tile_counters, dtype, scale: as for cakv_local_shard_forward.
+ * out, lse, workspace, workspace_bytes, tile_counters, dtype, scale: as for
+ *   cakv_local_shard_forward (the workspace size query takes Tq).
  * Errors: as for cakv_block_update, plus n_blocks outside
  * [1, CAKV_MAX_CHUNKS], a block length outside [0, 2^31 - 1], a NULL block
  * pointer that would be read.
@@ -247,7 +260,18 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
                                 const int64_t* kv_off_host, int n_blocks, int dtype, int B,
                                 int Hq, int Hkv, int Tq, int D, int64_t q_offset, int causal,
                                 float scale, void* out, int out_dtype, float* lse,
+                                void* workspace, int64_t workspace_bytes,
                                 int64_t* tile_counters, void* stream);
+
+/*
+ * Bytes of workspace that lets cakv_local_shard_forward (Tq = chunk_len) or
+ * cakv_forward_blocks split the key range of a small share (written to the
+ * HOST int64 *bytes_host); 0 when the share fills the GPU without splitting.
+ * Errors: NULL bytes_host, and the size and dtype checks of
+ * cakv_block_update.
+ */
+cakv_status cakv_forward_workspace_size(int dtype, int B, int Hq, int Hkv, int Tq, int D,
+                                        int64_t* bytes_host);
 
 /*
  * Gradients of cakv_forward_blocks for training (the pages apply sequence

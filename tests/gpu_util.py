@@ -59,13 +59,16 @@ class Inputs:
         self.qd = {r: to_dev(self.q[r]) for r in self.ranks}
 
 
-def run_forward(inp: Inputs, rank: int, out_dtype=torch.float32, counters=False):
+def run_forward(inp: Inputs, rank: int, out_dtype=torch.float32, counters=False,
+                workspace="auto"):
+    """The whole-shard call; workspace="auto" lets small shares take the
+    key-split path, None keeps the single-pass path."""
     w = inp.w
     out = torch.empty((w.B, w.C, w.Hq, w.D), dtype=out_dtype, device="cuda")
     lse = torch.empty((w.B, w.Hq, w.C), dtype=torch.float32, device="cuda")
     tc = torch.zeros(3, dtype=torch.int64, device="cuda") if counters else None
     cakv.cakv_local_shard_forward(inp.qd[rank], inp.kb, inp.vb, rank, w.causal, out, lse,
-                                  tile_counters=tc)
+                                  tile_counters=tc, workspace=workspace)
     torch.cuda.synchronize()
     return out, lse, tc
 

@@ -143,20 +143,22 @@ def _fwd(**kw):
     n = kw.pop("n", 4)
     kb = (ctypes.c_void_p * n)(*([FAKE] * n))
     args = dict(q=FAKE, kb=kb, vb=kb, dtype=1, B=1, Hq=8, Hkv=8, C=64, n=n, D=128, rank=3,
-                causal=1, scale=0.0, out=FAKE, odt=0, lse=None, tc=None, st=None)
+                causal=1, scale=0.0, out=FAKE, odt=0, lse=None, ws=None, wsb=0, tc=None,
+                st=None)
     args.update(kw)
     return L.cakv_local_shard_forward(args["q"], args["kb"], args["vb"], args["dtype"],
                                       args["B"], args["Hq"], args["Hkv"], args["C"], args["n"],
                                       args["D"], args["rank"], args["causal"], args["scale"],
-                                      args["out"], args["odt"], args["lse"], args["tc"],
-                                      args["st"])
+                                      args["out"], args["odt"], args["lse"], args["ws"],
+                                      args["wsb"], args["tc"], args["st"])
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(rank=4), 5), (dict(rank=-1), 5), (dict(n=0, rank=0), 5), (dict(n=65, rank=0), 5),
     (dict(dtype=2), 3), (dict(odt=5), 3), (dict(D=32), 2), (dict(Hq=6, Hkv=4), 2),
     (dict(C=-1), 2), (dict(q=NULL), 1), (dict(out=NULL), 1), (dict(kb=None), 1),
-    (dict(out=MIS), 4), (dict(q=MIS), 4),
+    (dict(out=MIS), 4), (dict(q=MIS), 4), (dict(ws=MIS, wsb=1 << 20), 4),
+    (dict(ws=FAKE, wsb=-1), 2),
 ])
 def test_local_shard_errors(kw, code):
     assert _fwd(**kw) == code
@@ -271,6 +273,28 @@ def test_decode_noalloc_errors_and_scratch_limit():
         assert nb.value <= cakv.CAKV_DECODE_SCRATCH_BYTES
 
 
+def test_forward_workspace_size():
+    """Small bf16 shares of the four-wave kernel get a split workspace sized
+    S x rows x (D + 2) floats (S key parts, partial m, l, o per row); shares
+    that fill the GPU, fp32 and grouped-query d = 128 shapes need none."""
+    nb = ctypes.c_int64(-1)
+    # 8 heads x 2048 rows, d = 128: 128 four-wave workgroups -> 4 parts
+    assert L.cakv_forward_workspace_size(1, 1, 8, 8, 2048, 128, ctypes.byref(nb)) == 0
+    rows = 8 * 2048
+    assert nb.value == (2 * 4 * rows + 4 * rows * 128) * 4
+    assert L.cakv_forward_workspace_size(1, 64, 12, 12, 512, 64, ctypes.byref(nb)) == 0
+    assert nb.value == 0                        # 3,072 workgroups: no split
+    assert L.cakv_forward_workspace_size(0, 1, 8, 8, 2048, 128, ctypes.byref(nb)) == 0
+    assert nb.value == 0                        # fp32
+    assert L.cakv_forward_workspace_size(1, 1, 32, 8, 4096, 128, ctypes.byref(nb)) == 0
+    assert nb.value == 0                        # grouped heads at d = 128 (ping-pong kernel)
+    assert L.cakv_forward_workspace_size(1, 1, 8, 8, 0, 128, ctypes.byref(nb)) == 0
+    assert nb.value == 0
+    assert L.cakv_forward_workspace_size(2, 1, 8, 8, 64, 128, ctypes.byref(nb)) == 3
+    assert L.cakv_forward_workspace_size(1, 1, 8, 8, 64, 96, ctypes.byref(nb)) == 2
+    assert L.cakv_forward_workspace_size(1, 1, 8, 8, 64, 128, None) == 1
+
+
 def test_forward_blocks_errors():
     I64 = ctypes.c_int64
     lens = (I64 * 2)(100, 0)
@@ -279,7 +303,7 @@ def test_forward_blocks_errors():
 
     def fb(q=FAKE, n=2, dtype=1, B=1, D=128, Hkv=2, out=FAKE, odt=0, ln=lens, k=ptrs):
         return L.cakv_forward_blocks(q, k, ptrs, ln, offs, n, dtype, B, 8, Hkv, 50, D, 100, 1, 0.0,
-                                     out, odt, None, None, None)
+                                     out, odt, None, None, 0, None, None)
     assert fb(dtype=5) == 3
     assert fb(odt=5) == 3
     assert fb(n=0) == 5

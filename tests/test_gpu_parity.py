@@ -120,3 +120,41 @@ def test_bf16_output_copy():
     out16, lse16, _ = run_forward(inp, 2, out_dtype=torch.bfloat16)
     assert torch.equal(out16, out32.to(torch.bfloat16))
     assert torch.equal(lse16, lse32)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, Hq, Hkv, T, N, D, causal, ranks): four-wave shapes whose grids leave
+    # resident slots empty, so the whole-shard call cuts each query tile's
+    # key range into parts combined by log-sum-exp
+    (1, 8, 8, 8192, 4, 128, True, (0, 3)),      # the sharp-head shares: 4 parts
+    (1, 8, 8, 1024, 4, 128, True, (1, 2)),      # 8 parts, some with no tile
+    (2, 3, 3, 3 * 333, 3, 64, False, (0,)),     # d = 64, bidirectional, ragged tail
+    (1, 2, 2, 2 * 45, 2, 128, True, (0, 1)),    # fewer tiles than parts
+])
+def test_small_grid_key_split(case):
+    """The split path (workspace given) and the single-pass path (no
+    workspace) both meet the oracle, and count the same tiles as it."""
+    B, Hq, Hkv, T, N, D, causal, ranks = case
+    k_mul = tuple(8.0 if g >= Hkv // 2 else 1.0 for g in range(Hkv)) if T == 8192 else None
+    w = syn.Workload("split", B=B, Hq=Hq, Hkv=Hkv, T=T, N=N, D=D, dtype="bf16", causal=causal,
+                     ranks=ranks, k_head_mul=k_mul, seed=91)
+    import context_attention_kv_amd as cakv
+    nbytes = cakv.cakv_forward_workspace_size(cakv.CAKV_BF16, B, Hq, Hkv, w.C, D)
+    assert nbytes > 0, "the case was meant to take the split path"
+    inp = Inputs(w)
+    for r in ranks:
+        rows = all_rows(B, Hq, w.C) if w.C <= 1024 else syn.sample_rows(w, per_head=64, seed=r)
+        ref_o, ref_l = oracle_rows(inp, r, rows)
+        tiles = []
+        for ws in ("auto", None):
+            out = torch.empty((B, w.C, Hq, D), dtype=torch.float32, device="cuda")
+            lse = torch.empty((B, Hq, w.C), dtype=torch.float32, device="cuda")
+            tc = torch.zeros(3, dtype=torch.int64, device="cuda")
+            cakv.cakv_local_shard_forward(inp.qd[r], inp.kb, inp.vb, r, causal, out, lse,
+                                          tile_counters=tc, workspace=ws)
+            torch.cuda.synchronize()
+            got_o, got_l = gather_rows(out, lse, rows)
+            compare(got_o, got_l, ref_o, ref_l, "bf16",
+                    f"split case {case} rank {r} workspace={ws}", rows)
+            tiles.append(tc.cpu().tolist())
+        assert tiles[0] == tiles[1] == list(expected_tiles(w, r)), tiles
