@@ -200,11 +200,13 @@ def launch_stats(ms):
 
 def forward_kernel_name(w) -> str:
     """The forward kernel the library launches for this workload: fp32 inputs
-    go to the fp32 kernel; bf16 grouped-query shares at d=128 to the ping-pong
-    kernel, every other bf16 shape to the four-wave kernel."""
+    go to the fp32 kernel; bf16 at d = 64, and one query head per kv head on
+    fewer than 2,048 32-row tasks, to the four-wave kernel; every other bf16
+    shape to the ping-pong kernel."""
     if w.dtype != "bf16":
         return "fwd_f32_kernel"
-    if w.D == 64 or w.Hq == w.Hkv:
+    tasks = w.B * w.Hq * ((w.C + 31) // 32)
+    if w.D == 64 or (w.Hq == w.Hkv and tasks < 2048):
         return "fwd_bf16_4w_kernel"
     return "fwd_bf16_kernel"
 

@@ -78,8 +78,8 @@ cakv_status set_grid(cakv::FwdArgs& a, int dtype, int D) {
     long long per_bg, n_wg;
     if (dtype == CAKV_BF16) {
         const long long G = a.Hq / a.Hkv;
-        const long long nw = cakv::fwd_bf16_waves(D, (int)G);
         const long long npblk = (a.Tq + 31LL) / 32;   // 32 query rows per wave
+        const long long nw = cakv::fwd_bf16_waves(D, (int)G, (long long)a.B * a.Hq * npblk);
         per_bg = (G * npblk + nw - 1) / nw;
         n_wg = (long long)a.B * a.Hkv * per_bg;
     } else {
@@ -106,7 +106,7 @@ SplitPlan split_plan(int dtype, int B, int Hq, int Hkv, int Tq, int D) {
     SplitPlan p{1, (long long)B * Hq * Tq, 0};
     if (dtype != CAKV_BF16 || p.rows == 0) return p;
     const long long G = Hq / Hkv;
-    const long long nw = cakv::fwd_bf16_waves(D, (int)G);
+    const long long nw = cakv::fwd_bf16_waves(D, (int)G, (long long)B * Hq * ((Tq + 31LL) / 32));
     if (nw != 4) return p;   // only the four-wave kernel splits
     const long long per_bg = (G * ((Tq + 31LL) / 32) + nw - 1) / nw;
     const long long n_wg = (long long)B * Hkv * per_bg;

@@ -48,7 +48,9 @@ struct FwdArgs {
 // Launchers (return the hipError_t of the launch as int).
 int launch_fwd_bf16(const FwdArgs& a, int D, void* stream);
 int launch_fwd_f32(const FwdArgs& a, int D, void* stream);
-int fwd_bf16_waves(int D, int G);   // waves per workgroup (32 query rows each) for D, G = Hq / Hkv
+// waves per workgroup (32 query rows each) of the kernel that serves D, G =
+// Hq / Hkv and `tasks` = B * Hq * ceil(Tq / 32) wave tasks
+int fwd_bf16_waves(int D, int G, long long tasks);
 int fwd_f32_wg_rows();
 
 int launch_state_init(float* m, float* l, float* o, long long rows, int D, void* stream);

@@ -35,11 +35,12 @@
 //   * workgroup ids are remapped so that each XCD works through a contiguous
 //     range of (batch, kv head) pairs (their K/V stream then hits that XCD's
 //     L2), heaviest query tiles first.
-// That ping-pong kernel serves grouped-query shares at d = 128. Every other
-// shape (d = 64; d = 128 with one query head per kv head) goes to a four-wave
-// kernel with the same tile arithmetic: one wave per SIMD, several
-// workgroups per CU running free of each other, a double buffer of tiles and
-// one barrier per tile (fwd_bf16_4w_kernel below).
+// That ping-pong kernel serves d = 128 shares whose grid fills the CUs. The
+// others (d = 64; small d = 128 grids with one query head per kv head) go to
+// a four-wave kernel with the same tile arithmetic: one wave per SIMD,
+// several workgroups per CU running free of each other, a double buffer of
+// tiles and one barrier per tile (fwd_bf16_4w_kernel below), which cuts the
+// key range of small grids into parts merged by log-sum-exp.
 #include <hip/hip_runtime.h>
 
 #include "fwd_args.h"
@@ -978,11 +979,18 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     }
 }
 
-// Which kernel serves a shape: the ping-pong kernel for grouped-query shares
-// at d = 128 (measured faster there: 1,039 against 910 TFLOP/s on the
-// million-token share), the four-wave kernel otherwise (d = 64 bidirectional
-// +43 %, small d = 128 shares +36 %, the B=8 H=64 T=32768 share +4 %).
-bool use_four_waves(int D, int G) { return D == 64 || G == 1; }
+// Which kernel serves a shape: the ping-pong kernel at d = 128 (grouped
+// query heads: 1,039 against 910 TFLOP/s on the million-token share), the
+// four-wave kernel at d = 64 (bidirectional share +43 %) and for small grids
+// (which it also splits by key range, more workgroups than CUs).
+// tasks = 32-row wave tasks of the launch (B * Hq * ceil(Tq / 32)).
+bool use_four_waves(int D, int G, long long tasks) {
+    if (D == 64) return true;
+    // one query head per kv head: the ping-pong kernel once its grid fills
+    // the CUs (one 8-wave workgroup each; 1,105 against 1,012 TFLOP/s on the
+    // B8 H64 T32768 share), the four-wave kernel with key splits below that
+    return G == 1 && tasks < 256LL * Cfg<128>::NW;
+}
 
 // Combine the S partial states of each row (log-sum-exp rule in log2 units):
 // M = max_s m_s, L = sum_s 2^(m_s - M) l_s, out = sum_s 2^(m_s - M) o_s / L,
@@ -1028,7 +1036,7 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const FwdArgs a) {
 template <int D>
 int launch(const FwdArgs& a, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (use_four_waves(D, a.Hq / a.Hkv)) {
+    if (use_four_waves(D, a.Hq / a.Hkv, (long long)a.B * a.Hq * ((a.Tq + 31) / 32))) {
         const unsigned grid = (unsigned)((long long)a.n_wg * a.n_split);
         if (a.counters)
             hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, true>), dim3(grid), dim3(256), 0, s, a);
@@ -1051,7 +1059,9 @@ int launch(const FwdArgs& a, void* stream) {
 
 }  // namespace
 
-int fwd_bf16_waves(int D, int G) { return use_four_waves(D, G) ? 4 : Cfg<128>::NW; }
+int fwd_bf16_waves(int D, int G, long long tasks) {
+    return use_four_waves(D, G, tasks) ? 4 : Cfg<128>::NW;
+}
 
 int launch_fwd_bf16(const FwdArgs& a, int D, void* stream) {
     if (D == 128) return launch<128>(a, stream);

@@ -19,7 +19,9 @@ static int no_launch() { return (int)hipErrorNotSupported; }
 
 int launch_fwd_bf16(const FwdArgs&, int, void*) { return no_launch(); }
 int launch_fwd_f32(const FwdArgs&, int, void*) { return no_launch(); }
-int fwd_bf16_waves(int D, int G) { return (D == 64 || G == 1) ? 4 : 8; }
+int fwd_bf16_waves(int D, int G, long long tasks) {
+    return (D == 64 || (G == 1 && tasks < 256LL * 8)) ? 4 : 8;
+}
 int fwd_f32_wg_rows() { return 64; }
 int launch_state_init(float*, float*, float*, long long, int, void*) { return no_launch(); }
 int launch_counter_add(unsigned long long*, unsigned long long, void*) { return no_launch(); }
