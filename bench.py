@@ -351,13 +351,15 @@ def bench_backward(args):
     steps = max(args.steps, 1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    clock = ClockSampler()
+    with clock:
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     flops = 2.5 * useful_flops(w, [r])
     tf = flops / (ms * 1e-3) / 1e12
@@ -380,7 +382,8 @@ def bench_backward(args):
                      "achieved": round(tf, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": backward_traffic(w.name),
-                     "avg_call_ms": round(ms, 4), "flops_per_call": flops},
+                     "avg_call_ms": round(ms, 4), "flops_per_call": flops,
+                     "gfx_clock": clock.summary()},
     }
     print(json.dumps(rec), flush=True)
 

@@ -465,7 +465,7 @@ cakv_status cakv_forward_workspace_size(int dtype, int B, int Hq, int Hkv, int T
 cakv_status cakv_backward_workspace_size(int B, int Hq, int Tq, int64_t* bytes_host) {
     if (!bytes_host) return fail(CAKV_ERR_NULL, "bytes_host is NULL");
     if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
-    *bytes_host = (int64_t)B * Hq * Tq * 8;   // delta, then lse in log2 units
+    *bytes_host = (int64_t)B * Hq * Tq * 8;   // -delta, then -lse / scale, per row
     return ok();
 }
 
@@ -536,8 +536,8 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
     a.scale = resolve_scale(scale, D);
     a.scale_log2 = a.scale * 1.4426950408889634f;
     a.causal = causal ? 1 : 0;
-    a.delta = static_cast<float*>(workspace);
-    a.lse2 = a.delta + (long long)B * Hq * Tq;
+    a.ndelta = static_cast<float*>(workspace);
+    a.nlse = a.ndelta + (long long)B * Hq * Tq;
     a.dq = dq;
     const int G = Hq / Hkv;
     const long long npblk = (Tq + 31) / 32;

@@ -23,15 +23,15 @@ struct BwdArgs {
     float* dv[CAKV_MAX_CHUNKS];
     long long kv_off[CAKV_MAX_CHUNKS];
     int kv_len[CAKV_MAX_CHUNKS];
-    int kt0[CAKV_MAX_CHUNKS + 1];           // first 128-key tile of block t; kt0[n] = total
+    int kt0[CAKV_MAX_CHUNKS + 1];           // first kBwdKeyTile-key tile of block t; kt0[n] = total
     int n_blocks;
     int B, Hq, Hkv, Tq;
     long long q_off;
     float scale;                            // score scale
     float scale_log2;                       // scale * log2(e)
     int causal;
-    float* delta;                           // [B, Hq, Tq] workspace: rowsum(dout * out)
-    float* lse2;                            // [B, Hq, Tq] workspace: lse * log2(e), +inf for -inf
+    float* ndelta;                          // [B, Hq, Tq] workspace: -rowsum(dout * out)
+    float* nlse;                            // [B, Hq, Tq] workspace: -lse / scale, -inf for a row without keys
     float* dq;                              // [B, Tq, Hq, D] fp32
     int wg_per_bg;                          // dq kernel: workgroups per (batch, kv head)
 };

@@ -175,8 +175,10 @@ __device__ __forceinline__ int xcd_logical(int bid, int n) {
 }
 
 // ---------------------------------------------------------------- delta
-// delta and the row's lse in log2 units (+inf for a row without keys, so that
-// every p of that row is 0), per query row
+// Per query row, negated: -delta and -lse / scale (-inf for a row without
+// keys, so that every p of that row is 0). The dk/dv kernel starts its S and
+// dP accumulators from them, so that its products give s - lse / scale and
+// dP - delta directly.
 template <int D>
 __global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
     constexpr int PER = D / 64;
@@ -194,9 +196,9 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const BwdArgs a) {
         const long long h = row % a.Hq, bi = row / a.Hq;
         const long long i = bi % a.Tq, b = bi / a.Tq;
         const long long si = (b * a.Hq + h) * a.Tq + i;
-        a.delta[si] = s;
+        a.ndelta[si] = -s;
         const float l = a.lse[si];
-        a.lse2[si] = l == -INFINITY ? INFINITY : l * kLog2e;
+        a.nlse[si] = l == -INFINITY ? -INFINITY : -l / a.scale;
     }
 }
 
@@ -246,7 +248,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
         const long long si = ((long long)b * a.Hq + h) * a.Tq + row;
         const float l = a.lse[si];
         lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-        dlt = a.delta[si];
+        dlt = -a.ndelta[si];
     }
     f32x16 dq_acc[C::DB];
 #pragma unroll
@@ -413,7 +415,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     constexpr int QR = 32, TB = QR * C::ROW_BYTES;
     constexpr int REG = TB / 1024;                // 1 KB regions per Q (or dO) tile
     constexpr int VT = kBwdKeyTile * C::ROW_BYTES;   // the workgroup's V rows
-    // [V rows] then 2 x [Q | dO | lse (64 floats) | delta (64 floats) | pad]
+    // [V rows] then 2 x [Q | dO | -lse/scale (64 floats) | -delta (64 floats) | pad]
     constexpr int BUF = 2 * TB + 1024;
     __shared__ __attribute__((aligned(1024))) char smem[VT + 2 * BUF];
     const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
@@ -439,6 +441,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     const bool key_ok = key < len;
     const long long wg_first_kpos = a.kv_off[blk] + wkey0;
     const int lane_rel = 16 * hh - wkey;   // row 16hh of a tile minus this lane's key, relative
+    const bool wave_keys_all = wkey0 + 32 * wave + 32 <= len;   // all 32 keys of the wave present
     const long long q_rs = (long long)a.Hq * D, kv_rs = (long long)a.Hkv * D;
 
     // K^T (B operand): lane (l32, hh) holds K[key][16s + 8hh .. +7]
@@ -483,7 +486,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     while (rt0 < nrt && !tile_ok(rt0)) ++rt0;
     const int nq = (nrt - rt0) * G;   // query tiles to visit: (head, row block)
     // copy n of this wave fills 1 KB region 4n + wave of the Q and of the dO
-    // tile; waves 0 and 1 also copy the tile's 32 lse and delta values
+    // tile; waves 0 and 1 also copy the tile's 32 -lse/scale and -delta values
     const unsigned cp_off = region_off<D>(wave < REG ? wave : 0, lane, q_rs);
     // query tiles go head-fastest: tile n is head n % G of row block
     // rt0 + n / G; running counters instead of divisions
@@ -506,7 +509,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
         }
         if (wave < 2) {
             const long long si = ((long long)b * a.Hq + h) * a.Tq + r0;
-            const i32x4 rs = make_rsrc(wave == 0 ? a.lse2 + si : a.delta + si, (unsigned)(rows * 4));
+            const i32x4 rs = make_rsrc(wave == 0 ? a.nlse + si : a.ndelta + si, (unsigned)(rows * 4));
             copy4_to_lds(rs, (unsigned)(4 * lane), dst + 2 * TB + 256 * wave);
         }
     };
@@ -531,12 +534,22 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
         const lds_char* qt = (const lds_char*)smem + VT + buf * BUF;
         const lds_char* dt = qt + TB;
         {
-            // S = Q K^T, dP = dO V^T: s[r] = score(row r0 + 16hh + r, key)
+            // S = Q K^T - lse / scale, dP = dO V^T - delta, from accumulators
+            // that start at the rows' -lse / scale and -delta (copied with
+            // the tile): s[r] belongs to row r0 + 16hh + r and this lane's key
             f32x16 s, dp;
+            {
+                const lds_char* lt = qt + 2 * TB + 64 * hh;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[r] = 0.f;
-                dp[r] = 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 l4 = *(const lds_f32x4*)(lt + 16 * i);
+                    const f32x4 d4 = *(const lds_f32x4*)(lt + 256 + 16 * i);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        s[4 * i + k] = l4[k];
+                        dp[4 * i + k] = d4[k];
+                    }
+                }
             }
             const lds_char* vst = (const lds_char*)smem;
             __builtin_amdgcn_s_setprio(1);   // products first on a shared SIMD
@@ -562,29 +575,27 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
             // allowed: key present and (causal) at or before the row's
             // position: r + dlo >= 0, dlo = position of row 16hh minus this
             // lane's key (the tile's part is scalar, clamped to 32 bits), or
-            // +-2^30 for every / no row
-            int dlo = a.causal ? c_tq + lane_rel : (1 << 30);
-            if (!key_ok) dlo = -(1 << 30);
+            // +-2^30 for every / no row. Only tiles where some score is not
+            // allowed (the wave's last keys, the causal diagonal) apply the
+            // mask, as s = -inf (p = 0); the rest skip it (wave-uniform test:
+            // the wave's largest key is 32 wave + 31)
+            if (!wave_keys_all || (a.causal && c_tq < 32 * wave + 31)) {
+                int dlo = a.causal ? c_tq + lane_rel : (1 << 30);
+                if (!key_ok) dlo = -(1 << 30);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = r + dlo >= 0 ? s[r] : -INFINITY;
+            }
             u32x4 pb[2], dsb[2];
+            // p = e^{scale (s_ij - lse_i / scale)}, ds = p (dP - delta)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                // lse (log2 units) and delta of rows 16hh + 8j .. +7 (the same
-                // for every lane of a half)
-                const int ro = 4 * (16 * hh + 8 * j);
-                const f32x4 l0 = *(const lds_f32x4*)(qt + 2 * TB + ro);
-                const f32x4 l1 = *(const lds_f32x4*)(qt + 2 * TB + ro + 16);
-                const f32x4 d0 = *(const lds_f32x4*)(qt + 2 * TB + 256 + ro);
-                const f32x4 d1 = *(const lds_f32x4*)(qt + 2 * TB + 256 + ro + 16);
                 f32x8 p8, d8;
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int r = 8 * j + u;
-                    const float l = u < 4 ? l0[u] : l1[u - 4];
-                    const float dr = u < 4 ? d0[u] : d1[u - 4];
-                    const float e = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -l));
-                    const float p = r + dlo >= 0 ? e : 0.f;
+                    const float p = fast_exp2(s[r] * a.scale_log2);
                     p8[u] = p;
-                    d8[u] = p * (dp[r] - dr);
+                    d8[u] = p * dp[r];
                 }
                 pb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(p8, bf16x8));
                 dsb[j] = __builtin_bit_cast(u32x4, __builtin_convertvector(d8, bf16x8));

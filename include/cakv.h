@@ -291,7 +291,7 @@ cakv_status cakv_forward_workspace_size(int dtype, int B, int Hq, int Hkv, int T
  *   device pointers, block t = [B, kv_len_host[t], Hkv, D] fp32. All outputs
  *   are overwritten (a block no query sees gets zeros).
  * workspace: device buffer of cakv_backward_workspace_size bytes (per
- *   row: delta = dout . out and the lse in log2 units), 16-byte aligned,
+ *   row: -delta = -dout . out and -lse / scale), 16-byte aligned,
  *   owned by the caller.
  * Errors: CAKV_ERR_DTYPE unless dtype = CAKV_BF16; otherwise as for
  * cakv_forward_blocks, plus NULL out / lse / dout / dq / gradient block
