@@ -36,6 +36,7 @@ EXPORTED = (
     "cakv_lse_merge", "cakv_local_shard_forward", "cakv_diag_mfma_burn", "cakv_decode",
     "cakv_decode_workspace_size", "cakv_forward_blocks", "cakv_backward_blocks",
     "cakv_backward_workspace_size", "cakv_decode_noalloc", "cakv_forward_workspace_size",
+    "cakv_diag_set_workgroup_order",
 )
 CAKV_DECODE_SCRATCH_BYTES = 32 << 20   # scratch array behind cakv_decode_noalloc
 DIAG_MFMA_WG = 2048   # workgroups of one cakv_diag_mfma_burn launch (include/cakv_diag.h)
@@ -74,6 +75,7 @@ def _load_lib():
         "cakv_local_shard_forward": ([P, P, P, I, I, I, I, I, I, I, I, I, F, P, I, P, P, I64, P, P],
                                      I),
         "cakv_diag_mfma_burn": ([I, I64, P, P], I),
+        "cakv_diag_set_workgroup_order": ([I], I),
         "cakv_decode": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P], I),
         "cakv_forward_blocks": ([P, P, P, P, P, I, I, I, I, I, I, I, I64, I, F, P, I, P, P, I64, P,
                                  P], I),
@@ -268,6 +270,13 @@ def cakv_diag_mfma_burn(zero_operands: bool, iters: int, sink, stream=None):
     unit (random or zero operands); FLOPs = diag_mfma_flops(iters)."""
     _check(_lib.cakv_diag_mfma_burn(int(bool(zero_operands)), int(iters), _ptr(sink),
                                     _stream(stream)), "cakv_diag_mfma_burn")
+
+
+def cakv_diag_set_workgroup_order(order: int):
+    """Permute the logical workgroup ids of every later launch (0 none, 1
+    scrambled, 2 reversed): an ordering check for tests; results must stay
+    bit-identical."""
+    _check(_lib.cakv_diag_set_workgroup_order(int(order)), "cakv_diag_set_workgroup_order")
 
 
 def diag_mfma_flops(iters: int) -> float:

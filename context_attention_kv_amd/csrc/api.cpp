@@ -3,12 +3,15 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include "cakv.h"
 #include "cakv_diag.h"
@@ -19,6 +22,19 @@
 namespace {
 
 thread_local std::string g_err;
+// workgroup-order permutation the launchers apply (cakv_diag_set_workgroup_order)
+std::atomic<int> g_wg_order{0};
+
+// Named ranges for timeline tools (rocprofv3 --marker-trace): every entry
+// point that enqueues kernels is one range, and its enqueue step a range
+// inside it, so a timeline shows the host's checks and scheduling apart from
+// the launches. Nearly free when no tool is attached.
+struct Range {
+    explicit Range(const char* name) { roctxRangePushA(name); }
+    ~Range() { roctxRangePop(); }
+    Range(const Range&) = delete;
+    Range& operator=(const Range&) = delete;
+};
 
 cakv_status fail(cakv_status s, const char* fmt, ...) {
     char buf[512];
@@ -238,12 +254,14 @@ cakv_status cakv_schedule(int rank, int n_chunks, int64_t chunk_len, int causal,
 
 cakv_status cakv_state_init(float* m, float* l, float* o, int B, int Hq, int Tq, int D,
                             void* stream) {
+    const Range range("cakv_state_init");
     if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
     if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
     const long long rows = (long long)B * Hq * Tq;
     if (rows == 0) return ok();
     if (!m || !l || !o) return fail(CAKV_ERR_NULL, "state pointer is NULL");
     if (!aligned16(o)) return fail(CAKV_ERR_ALIGN, "o not 16-byte aligned");
+    const Range enq("enqueue");
     return hip_status(cakv::launch_state_init(m, l, o, rows, D, stream), "state_init launch");
 }
 
@@ -251,6 +269,7 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
                               int Hq, int Hkv, int Tq, int Tkv, int D, int64_t q_offset,
                               int64_t kv_offset, int causal, float scale, float* m, float* l,
                               float* o, int64_t* tile_counters, void* stream) {
+    const Range range("cakv_block_update");
     cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, Tkv, D);
     if (s != CAKV_OK) return s;
     if (B == 0 || Tq == 0) return ok();
@@ -275,6 +294,7 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
 
     cakv::FwdArgs a;
     std::memset(&a, 0, sizeof a);
+    a.wg_order = g_wg_order.load(std::memory_order_relaxed);
     a.q = q;
     a.k[0] = k;
     a.v[0] = v;
@@ -291,11 +311,13 @@ cakv_status cakv_block_update(const void* q, const void* k, const void* v, int d
     a.counters = reinterpret_cast<unsigned long long*>(tile_counters);
     s = set_grid(a, dtype, D);
     if (s != CAKV_OK) return s;
+    const Range enq("enqueue");
     return hip_status(launch_fwd(a, dtype, D, stream), "block_update launch");
 }
 
 cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* out,
                           int out_dtype, float* lse, int B, int Hq, int Tq, int D, void* stream) {
+    const Range range("cakv_finalize");
     if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
         return fail(CAKV_ERR_DTYPE, "out_dtype %d unknown", out_dtype);
     if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
@@ -303,6 +325,7 @@ cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* 
     if ((long long)B * Hq * Tq == 0) return ok();
     if (!m || !l || !o || !out) return fail(CAKV_ERR_NULL, "m, l, o or out is NULL");
     if (!aligned16(o) || !aligned16(out)) return fail(CAKV_ERR_ALIGN, "o/out not 16-byte aligned");
+    const Range enq("enqueue");
     return hip_status(cakv::launch_finalize(m, l, o, out, out_dtype == CAKV_BF16, lse, B, Hq, Tq,
                                             D, stream),
                       "finalize launch");
@@ -311,6 +334,7 @@ cakv_status cakv_finalize(const float* m, const float* l, const float* o, void* 
 cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_b,
                            const float* lse_b, float* o_out, float* lse_out, int B, int Hq,
                            int Tq, int D, void* stream) {
+    const Range range("cakv_lse_merge");
     if (B < 0 || Hq < 0 || Tq < 0) return fail(CAKV_ERR_SHAPE, "negative size");
     if (D != 64 && D != 128) return fail(CAKV_ERR_SHAPE, "D=%d unsupported (64 or 128)", D);
     if ((long long)B * Hq * Tq == 0) return ok();
@@ -318,6 +342,7 @@ cakv_status cakv_lse_merge(const float* o_a, const float* lse_a, const float* o_
         return fail(CAKV_ERR_NULL, "merge operand is NULL");
     if (!aligned16(o_a) || !aligned16(o_b) || !aligned16(o_out))
         return fail(CAKV_ERR_ALIGN, "o operands must be 16-byte aligned");
+    const Range enq("enqueue");
     return hip_status(cakv::launch_lse_merge(o_a, lse_a, o_b, lse_b, o_out, lse_out, B, Hq, Tq, D,
                                              stream),
                       "lse_merge launch");
@@ -330,6 +355,7 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
                                      int out_dtype, float* lse, void* workspace,
                                      int64_t workspace_bytes, int64_t* tile_counters,
                                      void* stream) {
+    const Range range("cakv_local_shard_forward");
     cakv_status s = check_common(dtype, B, Hq, Hkv, chunk_len, chunk_len, D);
     if (s != CAKV_OK) return s;
     if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
@@ -355,6 +381,7 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
 
     cakv::FwdArgs a;
     std::memset(&a, 0, sizeof a);
+    a.wg_order = g_wg_order.load(std::memory_order_relaxed);
     int n = 0;
     for (int t = 0; t < n_chunks; ++t) {
         if (cls[t] == CAKV_SKIP) {
@@ -388,6 +415,7 @@ cakv_status cakv_local_shard_forward(const void* q_local, const void* const* k_b
     s = set_grid(a, dtype, D);
     if (s != CAKV_OK) return s;
     apply_split(a, split_plan(dtype, B, Hq, Hkv, chunk_len, D), workspace, workspace_bytes);
+    const Range enq("enqueue");
     return hip_status(launch_fwd(a, dtype, D, stream), "local_shard_forward launch");
 }
 
@@ -398,6 +426,7 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
                                 float scale, void* out, int out_dtype, float* lse,
                                 void* workspace, int64_t workspace_bytes,
                                 int64_t* tile_counters, void* stream) {
+    const Range range("cakv_forward_blocks");
     cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
     if (s != CAKV_OK) return s;
     if (out_dtype != CAKV_F32 && out_dtype != CAKV_BF16)
@@ -420,6 +449,7 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
 
     cakv::FwdArgs a;
     std::memset(&a, 0, sizeof a);
+    a.wg_order = g_wg_order.load(std::memory_order_relaxed);
     int n = 0;
     for (int t = 0; t < n_blocks; ++t) {
         if (classify(q_offset, Tq, kv_off_host[t], kv_len_host[t], causal) == CAKV_SKIP) {
@@ -450,6 +480,7 @@ cakv_status cakv_forward_blocks(const void* q, const void* const* k_blocks_host,
     s = set_grid(a, dtype, D);
     if (s != CAKV_OK) return s;
     apply_split(a, split_plan(dtype, B, Hq, Hkv, Tq, D), workspace, workspace_bytes);
+    const Range enq("enqueue");
     return hip_status(launch_fwd(a, dtype, D, stream), "forward_blocks launch");
 }
 
@@ -477,6 +508,7 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
                                  const void* dout, float* dq, float* const* dk_blocks_host,
                                  float* const* dv_blocks_host, void* workspace,
                                  int64_t workspace_bytes, void* stream) {
+    const Range range("cakv_backward_blocks");
     cakv_status s = check_common(dtype, B, Hq, Hkv, Tq, 0, D);
     if (s != CAKV_OK) return s;
     if (dtype != CAKV_BF16) return fail(CAKV_ERR_DTYPE, "cakv_backward_blocks takes bf16 inputs only");
@@ -507,6 +539,7 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
 
     cakv::BwdArgs a;
     std::memset(&a, 0, sizeof a);
+    a.wg_order = g_wg_order.load(std::memory_order_relaxed);
     int kt = 0;
     for (int t = 0; t < n_blocks; ++t) {
         a.kt0[t] = kt;
@@ -550,6 +583,7 @@ cakv_status cakv_backward_blocks(const void* q, const void* const* k_blocks_host
         a.wg_per_bg = 0;
     }
     if (kt == 0 && Tq == 0) return ok();
+    const Range enq("enqueue");
     return hip_status(cakv::launch_bwd(a, D, stream), "backward launch");
 }
 
@@ -614,6 +648,7 @@ cakv_status decode_launch(const void* q, const void* const* k_portions_host,
     cakv_status s;
     cakv::DecArgs a;
     std::memset(&a, 0, sizeof a);
+    a.wg_order = g_wg_order.load(std::memory_order_relaxed);
     int tile = 0;
     for (int j = 0; j < n_portions; ++j) {
         a.tile0[j] = tile;
@@ -642,6 +677,7 @@ cakv_status decode_launch(const void* q, const void* const* k_portions_host,
     a.out = out;
     a.out_bf16 = out_dtype == CAKV_BF16;
     a.lse = lse;
+    const Range enq("enqueue");
     s = hip_status(cakv::launch_decode_split(a, D, stream), "decode split launch");
     if (s != CAKV_OK) return s;
     return hip_status(cakv::launch_decode_merge(a, D, stream), "decode merge launch");
@@ -657,6 +693,7 @@ cakv_status cakv_decode(const void* q, const void* const* k_portions_host,
                         int Hkv, int Tn, int D, int64_t q_off, int causal, float scale, void* out,
                         int out_dtype, float* lse, void* workspace, int64_t workspace_bytes,
                         void* stream) {
+    const Range range("cakv_decode");
     DecodePlan p;
     bool empty = false;
     cakv_status s = decode_check(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
@@ -677,6 +714,7 @@ cakv_status cakv_decode_noalloc(const void* q, const void* const* k_portions_hos
                                 const int64_t* kv_off_host, int n_portions, int dtype, int B,
                                 int Hq, int Hkv, int Tn, int D, int64_t q_off, int causal,
                                 float scale, void* out, int out_dtype, float* lse, void* stream) {
+    const Range range("cakv_decode_noalloc");
     DecodePlan p;
     bool empty = false;
     cakv_status s = decode_check(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
@@ -693,6 +731,12 @@ cakv_status cakv_decode_noalloc(const void* q, const void* const* k_portions_hos
     return decode_launch(q, k_portions_host, v_portions_host, kv_len_host, kv_off_host,
                          n_portions, B, Hq, Hkv, Tn, D, q_off, causal, scale, out, out_dtype, lse,
                          p, ws, stream);
+}
+
+cakv_status cakv_diag_set_workgroup_order(int order) {
+    if (order < 0 || order > 2) return fail(CAKV_ERR_RANGE, "workgroup order %d outside [0, 2]", order);
+    g_wg_order.store(order, std::memory_order_relaxed);
+    return ok();
 }
 
 cakv_status cakv_diag_mfma_burn(int zero_operands, int64_t iters, float* sink, void* stream) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "cakv.h"
+#include "wg_order.h"
 
 namespace cakv {
 
@@ -34,6 +35,8 @@ struct BwdArgs {
     float* nlse;                            // [B, Hq, Tq] workspace: -lse / scale, -inf for a row without keys
     float* dq;                              // [B, Tq, Hq, D] fp32
     int wg_per_bg;                          // dq kernel: workgroups per (batch, kv head)
+    int wg_order;                           // workgroup-order permutation (wg_order.h), 0 = none
+    int wg_mul, wg_add;                     // set by the launcher for each grid
 };
 
 int launch_bwd(const BwdArgs& a, int D, void* stream);

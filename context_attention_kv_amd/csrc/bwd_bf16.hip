@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(256, 2) bwd_dq_kernel(const BwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
 
-    const int logical = xcd_logical(blockIdx.x, gridDim.x);
+    const int logical = wg_permute(xcd_logical(blockIdx.x, gridDim.x), gridDim.x, a.wg_mul, a.wg_add);
     const int bg = logical / a.wg_per_bg;
     const int qt = a.wg_per_bg - 1 - logical % a.wg_per_bg;   // heaviest (latest rows) first
     const int b = bg / a.Hkv, g = bg % a.Hkv, G = a.Hq / a.Hkv;
@@ -424,7 +424,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     const int l32 = lane & 31, hh = lane >> 5;
 
     const int ntiles = a.kt0[a.n_blocks];
-    int id = xcd_logical(blockIdx.x, gridDim.x);   // key tiles of one head in order on one XCD
+    // key tiles of one head in order on one XCD
+    int id = wg_permute(xcd_logical(blockIdx.x, gridDim.x), gridDim.x, a.wg_mul, a.wg_add);
     const int kt = id % ntiles;
     id /= ntiles;
     const int g = id % a.Hkv, b = id / a.Hkv, G = a.Hq / a.Hkv;
@@ -659,12 +660,20 @@ int launch_all(const BwdArgs& a, void* stream) {
         if (e != hipSuccess) return (int)e;
     }
     if (n_dq > 0) {
-        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(256), 0, s, a);
+        BwdArgs aq = a;
+        const WgPerm pm = wg_perm(a.wg_order, n_dq);
+        aq.wg_mul = pm.mul;
+        aq.wg_add = pm.add;
+        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)n_dq), dim3(256), 0, s, aq);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
     if (n_kv > 0) {
-        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_kv), dim3(512), 0, s, a);
+        BwdArgs ak = a;
+        const WgPerm pm = wg_perm(a.wg_order, n_kv);
+        ak.wg_mul = pm.mul;
+        ak.wg_add = pm.add;
+        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)n_kv), dim3(512), 0, s, ak);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }

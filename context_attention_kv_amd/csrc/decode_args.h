@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "cakv.h"
+#include "wg_order.h"
 
 namespace cakv {
 
@@ -38,6 +39,8 @@ struct DecArgs {
     void* out;                              // [B, Tn, Hq, D] fp32 or bf16
     int out_bf16;
     float* lse;                             // [B, Hq, Tn] or null
+    int wg_order;                           // workgroup-order permutation (wg_order.h), 0 = none
+    int wg_mul, wg_add;                     // set by the launcher for the split grid
 };
 
 // Device address of this device's decode scratch array

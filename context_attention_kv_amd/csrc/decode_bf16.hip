@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(const DecArgs a) {
     const int l32 = lane & 31, hh = lane >> 5;
     const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
 
-    int id = xcd_logical(blockIdx.x, gridDim.x);
+    int id = wg_permute(xcd_logical(blockIdx.x, gridDim.x), gridDim.x, a.wg_mul, a.wg_add);
     const int rb = id % a.nrb;
     id /= a.nrb;
     const int g = id % a.Hkv;
@@ -463,8 +463,12 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(const DecArgs a) {
 
 }  // namespace
 
-int launch_decode_split(const DecArgs& a, int D, void* stream) {
-    const int grid = a.n_splits * a.B * a.Hkv * a.nrb;
+int launch_decode_split(const DecArgs& args, int D, void* stream) {
+    const int grid = args.n_splits * args.B * args.Hkv * args.nrb;
+    DecArgs a = args;
+    const WgPerm pm = wg_perm(a.wg_order, grid);
+    a.wg_mul = pm.mul;
+    a.wg_add = pm.add;
     if (D == 128)
         hipLaunchKernelGGL(decode_split_kernel<128>, dim3(grid), dim3(64), 0,
                            static_cast<hipStream_t>(stream), a);

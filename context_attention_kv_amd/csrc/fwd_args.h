@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "cakv.h"
+#include "wg_order.h"
 
 namespace cakv {
 
@@ -43,6 +44,8 @@ struct FwdArgs {
     float* split_m;                       // [n_split, rows] max, log2 units
     float* split_l;                       // [n_split, rows]
     float* split_o;                       // [n_split, rows, D] unnormalised
+    int wg_order;                         // workgroup-order permutation (wg_order.h), 0 = none
+    int wg_mul, wg_add;                   // set by the launcher for its grid
 };
 
 // Launchers (return the hipError_t of the launch as int).

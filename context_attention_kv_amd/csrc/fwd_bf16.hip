@@ -268,7 +268,7 @@ fwd_bf16_kernel(const FwdArgs a) {
     const int bid = blockIdx.x;
     const int per = a.n_wg / 8, rem = a.n_wg % 8;
     const int xcd = bid % 8, idx = bid / 8;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    const int logical = wg_permute(xcd * per + (xcd < rem ? xcd : rem) + idx, a.n_wg, a.wg_mul, a.wg_add);
     const int bg = logical / a.wg_per_bg;
     const int qt = a.wg_per_bg - 1 - (logical % a.wg_per_bg);  // heaviest first
     const int b = bg / a.Hkv, g = bg % a.Hkv;
@@ -665,7 +665,7 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     const int n_all = a.n_wg * S;
     const int per = n_all / 8, rem = n_all % 8;
     const int xcd = bid % 8, idx = bid / 8;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    const int logical = wg_permute(xcd * per + (xcd < rem ? xcd : rem) + idx, n_all, a.wg_mul, a.wg_add);
     const int sp = logical % S;
     const int lwg = logical / S;
     const int bg = lwg / a.wg_per_bg;
@@ -1034,10 +1034,14 @@ __global__ void __launch_bounds__(256) split_merge_kernel(const FwdArgs a) {
 }
 
 template <int D>
-int launch(const FwdArgs& a, void* stream) {
+int launch(const FwdArgs& args, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    FwdArgs a = args;   // the launcher fills in the workgroup-order permutation for its grid
     if (use_four_waves(D, a.Hq / a.Hkv, (long long)a.B * a.Hq * ((a.Tq + 31) / 32))) {
         const unsigned grid = (unsigned)((long long)a.n_wg * a.n_split);
+        const WgPerm pm = wg_perm(a.wg_order, grid);
+        a.wg_mul = pm.mul;
+        a.wg_add = pm.add;
         if (a.counters)
             hipLaunchKernelGGL((fwd_bf16_4w_kernel<D, true>), dim3(grid), dim3(256), 0, s, a);
         else
@@ -1050,8 +1054,14 @@ int launch(const FwdArgs& a, void* stream) {
                                dim3(256), 0, s, a);
         }
     } else if (a.counters) {
+        const WgPerm pm = wg_perm(a.wg_order, a.n_wg);
+        a.wg_mul = pm.mul;
+        a.wg_add = pm.add;
         hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0, s, a);
     } else {
+        const WgPerm pm = wg_perm(a.wg_order, a.n_wg);
+        a.wg_mul = pm.mul;
+        a.wg_add = pm.add;
         hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(a.n_wg), dim3(64 * Cfg<D>::NW), 0, s, a);
     }
     return (int)hipGetLastError();

@@ -48,8 +48,9 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
     const int lane = tid & (kRows - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kRows);
     const int nqt = (a.Tq + kRows - 1) / kRows;
-    const int qt = nqt - 1 - (int)(blockIdx.x % nqt);
-    const int bh = blockIdx.x / nqt;
+    const int wid = wg_permute((int)blockIdx.x, a.n_wg, a.wg_mul, a.wg_add);
+    const int qt = nqt - 1 - wid % nqt;
+    const int bh = wid / nqt;
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int g = h / (a.Hq / a.Hkv);
     const int row0 = qt * kRows;
@@ -255,8 +256,12 @@ __global__ void __launch_bounds__(kRows * kWaves) fwd_f32_kernel(const FwdArgs a
 
 int fwd_f32_wg_rows() { return kRows; }
 
-int launch_fwd_f32(const FwdArgs& a, int D, void* stream) {
+int launch_fwd_f32(const FwdArgs& args, int D, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
+    FwdArgs a = args;
+    const WgPerm pm = wg_perm(a.wg_order, a.n_wg);
+    a.wg_mul = pm.mul;
+    a.wg_add = pm.add;
     if (D == 128)
         hipLaunchKernelGGL(fwd_f32_kernel<128>, dim3(a.n_wg), dim3(kRows * kWaves), 0, st, a);
     else if (D == 64)

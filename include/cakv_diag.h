@@ -38,6 +38,20 @@ extern "C" {
  */
 cakv_status cakv_diag_mfma_burn(int zero_operands, int64_t iters, float* sink, void* stream);
 
+/*
+ * Ordering check (a test aid, not an operation of the method). Every kernel
+ * of the library maps its workgroup id to a unit of work (a query tile, a
+ * key tile, a key-range part, a decode split) and no workgroup waits for
+ * another, so every result must be the same whichever workgroup takes which
+ * unit. This sets, for the whole process, a permutation that the launchers
+ * apply to those logical ids from the next call on: order 0 (the default)
+ * none, 1 a scrambled order, 2 the reversed order. Results must stay
+ * bit-identical; order 1 and 2 give up the XCD-aware placement, so they are
+ * for tests only. Not synchronised with calls in flight on other threads.
+ * Errors: CAKV_ERR_RANGE for an order outside [0, 2].
+ */
+cakv_status cakv_diag_set_workgroup_order(int order);
+
 #ifdef __cplusplus
 }
 #endif

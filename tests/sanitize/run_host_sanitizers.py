@@ -41,7 +41,8 @@ def main():
     run(["g++", "-std=c++17", "-fPIC", "-shared", *SAN, "-D__HIP_PLATFORM_AMD__",
          "-I", "/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", csrc,
          os.path.join(csrc, "api.cpp"), os.path.join(HERE, "host_stubs.cpp"),
-         "-L", "/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", cakv])
+         "-L", "/opt/rocm/lib", "-lamdhip64", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib",
+         "-o", cakv])
     orc = os.path.join(OUT, "liboracle_san.so")
     run(["gcc", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math", *SAN,
          os.path.join(ROOT, "oracle", "oracle.c"), "-lm", "-o", orc])

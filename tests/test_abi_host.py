@@ -201,6 +201,17 @@ def test_diag_mfma_burn_errors():
     assert L.cakv_diag_mfma_burn(0, 0, None, None) == 0   # nothing to launch
 
 
+def test_diag_workgroup_order_range():
+    """Orders 0..2 are accepted (the launchers apply them from the next
+    call on; the GPU test checks results stay bit-identical); others are
+    rejected without changing the setting."""
+    for order in (1, 2, 0):
+        assert L.cakv_diag_set_workgroup_order(order) == 0
+    assert L.cakv_diag_set_workgroup_order(3) == 5    # CAKV_ERR_RANGE
+    assert L.cakv_diag_set_workgroup_order(-1) == 5
+    assert b"workgroup order" in L.cakv_last_error()
+
+
 def test_decode_errors_and_workspace_size():
     I64 = ctypes.c_int64
     lens = (I64 * 3)(1000, 0, 64)
