@@ -19,8 +19,8 @@
 //   S^T = K Q^T and dP^T = V dO^T on v_mfma_f32_32x32x16_bf16 (K, V as A
 //   operands, Q^T and dO^T in registers as B), dS = P (dP - delta), then
 //   dQ^T += K^T dS^T with K^T read through ds_read_b64_tr_b16.
-// bwd_dkdv_kernel: key-stationary, 8 waves of 32 keys (K^T in registers and
-//   the workgroup's 256 V rows in LDS, both B operands) over every 32-row
+// bwd_dkdv_kernel: key-stationary, 8 waves of 32 keys (K^T and V^T in
+//   registers, both B operands) over every 32-row
 //   query tile of the kv head's query heads, copied into LDS: S = Q K^T and
 //   dP = dO V^T (query rows in output registers), dV^T += dO^T P and
 //   dK^T += Q^T dS with dO^T and Q^T read through ds_read_b64_tr_b16.
@@ -414,10 +414,9 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     using C = BCfg<D>;
     constexpr int QR = 32, TB = QR * C::ROW_BYTES;
     constexpr int REG = TB / 1024;                // 1 KB regions per Q (or dO) tile
-    constexpr int VT = kBwdKeyTile * C::ROW_BYTES;   // the workgroup's V rows
-    // [V rows] then 2 x [Q | dO | -lse/scale (64 floats) | -delta (64 floats) | pad]
+    // 2 x [Q | dO | -lse/scale (64 floats) | -delta (64 floats) | pad]
     constexpr int BUF = 2 * TB + 1024;
-    __shared__ __attribute__((aligned(1024))) char smem[VT + 2 * BUF];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
     const unsigned lds0 = (unsigned)(unsigned long)(const lds_char*)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,9 +433,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     const int len = a.kv_len[blk];
     const int wkey0 = (kt - a.kt0[blk]) * kBwdKeyTile;   // the workgroup's first key
     // this lane's key: keys of the wave in the permuted order of the A-operand
-    // rows, so that the V rows it reads from LDS as a B operand are free of
-    // bank conflicts like the A reads (the order is the same everywhere: K^T,
-    // V^T, the mask and the dK, dV rows written)
+    // rows (the order is the same everywhere: K^T, V^T, the mask and the dK,
+    // dV rows written)
     const int wkey = 32 * wave + perm_row(l32);          // key within the workgroup's tile
     const int key = wkey0 + wkey;
     const bool key_ok = key < len;
@@ -445,27 +443,18 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     const bool wave_keys_all = wkey0 + 32 * wave + 32 <= len;   // all 32 keys of the wave present
     const long long q_rs = (long long)a.Hq * D, kv_rs = (long long)a.Hkv * D;
 
-    // K^T (B operand): lane (l32, hh) holds K[key][16s + 8hh .. +7]
-    u32x4 kf[C::DSTEPS];
+    // K^T and V^T (B operands) for the whole loop: lane (l32, hh) holds
+    // K[key][16s + 8hh .. +7] and V[key][16s + 8hh .. +7]; keys past the
+    // block's end are zeros
+    u32x4 kf[C::DSTEPS], vf[C::DSTEPS];
     {
         const long long ko = ((long long)b * len + (key_ok ? key : 0)) * kv_rs + (long long)g * D;
         const __bf16* kb_ = static_cast<const __bf16*>(a.k[blk]) + ko;
+        const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) + ko;
 #pragma unroll
-        for (int s = 0; s < C::DSTEPS; ++s)
+        for (int s = 0; s < C::DSTEPS; ++s) {
             kf[s] = key_ok ? *reinterpret_cast<const u32x4*>(kb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // the workgroup's V rows into LDS (swizzled tile; rows past the block's end zero)
-    {
-        constexpr int PER = kBwdKeyTile * C::UNITS / 512;
-        const __bf16* vb_ = static_cast<const __bf16*>(a.v[blk]) +
-                            ((long long)b * len + wkey0) * kv_rs + (long long)g * D;
-#pragma unroll
-        for (int n = 0; n < PER; ++n) {
-            const int c = tid + 512 * n;
-            const int row = c / C::UNITS, p = c % C::UNITS;
-            const u32x4 x = wkey0 + row < len ? *reinterpret_cast<const u32x4*>(vb_ + row * kv_rs + 8 * p)
-                                              : u32x4{0u, 0u, 0u, 0u};
-            *(lds_u32x4*)((lds_char*)smem + row * C::ROW_BYTES + 16 * (p ^ swz<D>(row))) = x;
+            vf[s] = key_ok ? *reinterpret_cast<const u32x4*>(vb_ + 16 * s + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
         }
     }
     f32x16 dk_acc[C::DB], dv_acc[C::DB];
@@ -516,7 +505,7 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
     };
     // the K and V loads above, in a form the compiler's wait tracking sees
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    if (nq > 0) issue(lds0 + VT);
+    if (nq > 0) issue(lds0);
     // the tile being computed: head c_hj of its group; c_tq = position of its
     // first row minus the workgroup's first key, saturated at 2^30 (with the
     // causal rule the first visited tile has c_tq >= -31, and it only grows)
@@ -531,8 +520,8 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
         const int buf = n & 1;
         // the other buffer was last read before the barrier that ended the
         // previous step
-        if (n + 1 < nq) issue(lds0 + VT + (buf ^ 1) * BUF);
-        const lds_char* qt = (const lds_char*)smem + VT + buf * BUF;
+        if (n + 1 < nq) issue(lds0 + (buf ^ 1) * BUF);
+        const lds_char* qt = (const lds_char*)smem + buf * BUF;
         const lds_char* dt = qt + TB;
         {
             // S = Q K^T - lse / scale, dP = dO V^T - delta, from accumulators
@@ -552,7 +541,6 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
                     }
                 }
             }
-            const lds_char* vst = (const lds_char*)smem;
             __builtin_amdgcn_s_setprio(1);   // products first on a shared SIMD
 #pragma unroll
             for (int st = 0; st < C::DSTEPS; ++st) {
@@ -560,16 +548,16 @@ __global__ void __launch_bounds__(512) bwd_dkdv_kernel(const BwdArgs a) {
                     as_bf16x8(tile_unit<D>(qt, perm_row(l32), 2 * st + hh)), as_bf16x8(kf[st]), s, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     as_bf16x8(tile_unit<D>(dt, perm_row(l32), 2 * st + hh)),
-                    as_bf16x8(tile_unit<D>(vst, wkey, 2 * st + hh)), dp, 0, 0, 0);
+                    as_bf16x8(vf[st]), dp, 0, 0, 0);
             }
-            // pipeline: one step's three operand reads ahead of its products
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            // pipeline: one step's two operand reads ahead of its products
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
             for (int f = 0; f < C::DSTEPS - 1; ++f) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_s_setprio(0);
