@@ -11,6 +11,8 @@ per-block ring (state init, one update per block, finalize, and a
 log-sum-exp merge); the backward; decode with a workspace and the
 allocation-free decode. The eager results of the forward cases are also held
 to the oracle on sampled rows, so the comparison is between right answers.
+A last case enqueues independent calls on two streams at once and checks
+that each result is the one the call gives alone.
 """
 import numpy as np
 import pytest
@@ -185,3 +187,66 @@ def test_decode_graph(noalloc):
     what = "allocation-free decode" if noalloc else "decode"
     say(f"{what} graph: B={B} Hq={Hq} Hkv={w.Hkv} hist={w.hist} Tn={Tn}")
     _replays_match(call, [out, lse], what)
+
+
+def test_calls_on_two_streams_at_once():
+    """Two whole-share forwards (each with its own workspace: the key-split
+    path) and a decode, enqueued on two streams of default priority so that
+    they can run at the same time: each result equals the same call run
+    alone, bit for bit (the library keeps no state between calls other than
+    the allocation-free decode's scratch, which this test does not use)."""
+    w = syn.Workload("two-streams", B=1, Hq=8, Hkv=8, T=4096, N=4, D=128, dtype="bf16",
+                     causal=True, ranks=(2, 3), seed=94)
+    inp = Inputs(w)
+    nb = cakv.cakv_forward_workspace_size(cakv.CAKV_BF16, 1, w.Hq, w.Hkv, w.C, w.D)
+    assert nb > 0
+
+    def fwd_bufs():
+        return (torch.empty((1, w.C, w.Hq, w.D), device="cuda"),
+                torch.empty((1, w.Hq, w.C), device="cuda"),
+                torch.empty(nb // 4 + 4, device="cuda"))
+
+    dw = syn.scaled(syn.DECODE_WORKLOADS[1], Tn=2)
+    q, k, v = syn.make_decode(dw)
+    bounds = dw.portions()
+    kd, vd = to_dev(k), to_dev(v)
+    kp = [kd[:, a:a + n].contiguous() for a, n in bounds]
+    vp = [vd[:, a:a + n].contiguous() for a, n in bounds]
+    offs = [a for a, _ in bounds]
+    qd = to_dev(q)
+    B, Tn, Hq, D = qd.shape
+
+    def dec_bufs():
+        need = cakv.cakv_decode_workspace_size(B, Hq, dw.Hkv, Tn, D, [t.shape[1] for t in kp])
+        return (torch.empty((B, Tn, Hq, D), device="cuda"), torch.empty((B, Hq, Tn), device="cuda"),
+                torch.empty(max(need, 16) // 4 + 4, device="cuda"))
+
+    def fwd(r, bufs, stream=None):
+        out, lse, ws = bufs
+        cakv.cakv_local_shard_forward(inp.qd[r], inp.kb, inp.vb, r, True, out, lse, workspace=ws,
+                                      stream=stream)
+
+    def dec(bufs, stream=None):
+        out, lse, ws = bufs
+        cakv.cakv_decode(qd, kp, vp, offs, dw.hist, True, out, lse, workspace=ws, stream=stream)
+
+    # alone, one after another
+    a2, a3, ad = fwd_bufs(), fwd_bufs(), dec_bufs()
+    fwd(2, a2)
+    fwd(3, a3)
+    dec(ad)
+    torch.cuda.synchronize()
+    # together: rank 2 and decode on one stream, rank 3 on the other
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    b2, b3, bd = fwd_bufs(), fwd_bufs(), dec_bufs()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        fwd(2, b2, stream=s1.cuda_stream)
+        fwd(3, b3, stream=s2.cuda_stream)
+        dec(bd, stream=s1.cuda_stream)
+    torch.cuda.synchronize()
+    say("two streams: forward ranks 2 and 3 and a decode, three rounds")
+    for what, x, y in (("rank 2", a2, b2), ("rank 3", a3, b3), ("decode", ad, bd)):
+        for j in range(2):
+            assert torch.equal(_bits(x[j]), _bits(y[j])), f"{what}: output {j} differs on two streams"
