@@ -156,11 +156,14 @@ int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
     return cakv::launch_fwd_f32(a, D, stream);
 }
 
-// Decode plan: how many splits the history's 32-key tiles are cut into.
-// About two rounds of resident waves over the chip (a wave holds 48 KB of LDS
-// at d=128, 24 KB at d=64: three or six per CU), each split at least one
-// tile; fewer, longer splits amortise each wave's first-tile wait (measured:
-// one or two rounds beat four by 3 %, eight by 8 %).
+// Decode plan: how many splits the history's 32-key tiles are cut into,
+// each split at least one tile. Few, long splits read the history fastest:
+// 768 waves in all (192 workgroups of four kv heads, on three quarters of the
+// CUs) when heads are grouped, 512 single-head waves otherwise. Measured on
+// the million-token history, one box, four-head workgroups: 512 waves
+// 5,958-5,969 GB/s, 640 6,696-6,710, 768 6,935-6,940, 896 6,819-6,822, 1,024
+// 6,738-6,747, 1,536 6,256-6,259 (another box: 2,048 6,115-6,154, 3,072
+// 6,068-6,074, 4,096 6,001-6,020); single-head waves 512 6,686, 1,536 5,957.
 struct DecodePlan {
     int nrb;               // 32-row blocks per (batch, kv head)
     long long tiles;       // tiles of all portions
@@ -192,7 +195,7 @@ cakv_status decode_plan(int B, int Hq, int Hkv, int Tn, int D, const int64_t* kv
     p->nrb = (int)((R + 31) / 32);
     p->tiles = tiles;
     const long long per_split = std::max(1LL, (long long)B * Hkv * p->nrb);
-    const long long waves = D == 128 ? 2 * 3 * 256 : 2 * 6 * 256;
+    const long long waves = cakv::decode_heads_per_wg(Hkv) > 1 ? 768 : 512;
     long long want = std::max(1LL, (waves + per_split - 1) / per_split);
     want = std::min(want, std::max(1LL, tiles));
     const long long tps = std::max(1LL, (tiles + want - 1) / want);

@@ -16,7 +16,8 @@ constexpr int kDecTile = 32;   // keys per decode tile
 // short) are numbered portion by portion; split s covers tiles
 // [s * tiles_per_split, (s + 1) * tiles_per_split). Wave (s, b, g, rb) folds
 // those tiles into an online-softmax state for row block rb (32 rows) of kv
-// head g of batch b and writes it to the workspace; the merge kernel then
+// head g of batch b and writes it to the workspace (a workgroup holds the
+// waves of decode_heads_per_wg neighbouring kv heads); the merge kernel then
 // combines the splits of every row.
 struct DecArgs {
     const void* q;                          // [B, Tn, Hq, D] bf16
@@ -48,6 +49,8 @@ struct DecArgs {
 // (the device current at the call), then cached. Returns a hipError_t as int.
 int decode_scratch_address(void** ptr);
 
+// kv heads per workgroup of the split kernel (one wave each) for Hkv heads
+inline int decode_heads_per_wg(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
 int launch_decode_split(const DecArgs& a, int D, void* stream);
 int launch_decode_merge(const DecArgs& a, int D, void* stream);
 

@@ -272,9 +272,11 @@ def test_decode_noalloc_errors_and_scratch_limit():
     assert dec(k=None) == 1
     assert dec(B=0, q=None, out=None) == 0   # nothing to do
     nb = I64(0)
-    assert L.cakv_decode_workspace_size(64, 32, 8, 16, 128, lens, 3, ctypes.byref(nb)) == 0
+    # 128 batch rows x 8 kv heads x two 32-row blocks: one split already needs
+    # 2,048 row blocks of state (34 MB)
+    assert L.cakv_decode_workspace_size(128, 32, 8, 16, 128, lens, 3, ctypes.byref(nb)) == 0
     assert nb.value > cakv.CAKV_DECODE_SCRATCH_BYTES
-    assert dec(B=64, Hq=32, Hkv=8, Tn=16) == 2
+    assert dec(B=128, Hq=32, Hkv=8, Tn=16) == 2
     assert "scratch" in L.cakv_last_error().decode()
     # the million-token history (32 query heads on 8, one to sixteen new
     # tokens) fits

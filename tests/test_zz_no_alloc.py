@@ -41,7 +41,7 @@ def _both(w, qd, kp, vp, offs):
 
 def test_noalloc_decode_equals_workspace_decode_twice():
     # first call: 4 batch rows, 32 query heads on 8, a 200,000-token history in
-    # 8 portions and 3 new tokens (split state ~25.6 MB of the 32 MiB array)
+    # 8 portions and 3 new tokens (split state ~12.8 MB of the 32 MiB array)
     big = _case(4, 32, 8, 200_000, 3, 8, 128, 2101)
     # second call, smaller: one batch row, 8 heads on 2, 1,000 tokens, d = 64
     small = _case(1, 8, 2, 1000, 2, 3, 64, 2102)
@@ -61,7 +61,7 @@ def test_noalloc_decode_equals_workspace_decode_twice():
 
 
 def test_noalloc_decode_rejects_sizes_above_its_scratch():
-    w = syn.DecodeWorkload("noalloc-big", B=64, Hq=32, Hkv=8, hist=1000, N=2, Tn=16, D=128,
+    w = syn.DecodeWorkload("noalloc-big", B=128, Hq=32, Hkv=8, hist=1000, N=2, Tn=16, D=128,
                            seed=2103)
     qd = torch.zeros((w.B, w.Tn, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
     kp = [torch.zeros((w.B, 500, w.Hkv, w.D), dtype=torch.bfloat16, device="cuda")
