@@ -194,3 +194,29 @@ def test_decode_random_shapes_sweep(i):
     ro, rl = _oracle_by_portions(q, k, v, bounds, hist, causal, rows)
     go, gl = gather_rows(out, lse, rows)
     compare(go, gl, ro, rl, "bf16", f"decode sweep {i}", rows)
+
+
+@pytest.mark.parametrize("case", [
+    # (B, Hq, Hkv, D, hist, Tn, causal, portions)
+    (2, 16, 8, 64, 3000, 5, True, [(1800, 700), (0, 900), (2500, 505), (900, 0), (900, 900)]),
+    (1, 8, 4, 128, 2500, 20, False, [(0, 1000), (1000, 1), (1001, 1519)]),
+    (3, 4, 4, 64, 900, 1, True, [(0, 901)]),
+])
+def test_decode_four_heads_per_workgroup(case):
+    """Shapes whose kv-head count is a multiple of four, which the split
+    kernel serves with four heads' waves per workgroup: d = 64 and 128, two
+    32-row blocks (Tn = 20 at G = 2), a tiny history with fewer tiles than
+    the plan's splits, portions shuffled and one empty, every row against
+    the oracle's per-portion attention merged by log-sum-exp."""
+    B, Hq, Hkv, D, hist, Tn, causal, bounds = case
+    say(f"decode, four heads per workgroup: B={B} Hq={Hq} Hkv={Hkv} D={D} hist={hist} "
+        f"Tn={Tn} causal={causal} portions={bounds}")
+    w = syn.DecodeWorkload("decode-hpw4", B=B, Hq=Hq, Hkv=Hkv, hist=hist, N=1, Tn=Tn, D=D,
+                           causal=causal, seed=7100 + B * 10 + Hkv)
+    q, k, v = syn.make_decode(w)
+    kp, vp = _portions_dev(k, v, bounds)
+    out, lse = _run(to_dev(q), kp, vp, [o for o, _ in bounds], hist, causal)
+    rows = all_rows(B, Hq, Tn)
+    ro, rl = _oracle_by_portions(q, k, v, bounds, hist, causal, rows)
+    go, gl = gather_rows(out, lse, rows)
+    compare(go, gl, ro, rl, "bf16", f"decode four heads per workgroup {case[:7]}", rows)
