@@ -741,7 +741,6 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
     const int v_dim = 16 * (g16 & 1) + 4 * (src & 3);
     const int v_sw = vswz<D>(src >> 2);
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the Q and state loads
     unsigned n_full = 0, n_masked = 0, n_skip = 0;
 
     // ---- tile sequence: blocks in the given (ring) order, 64 keys at a time ----
@@ -780,7 +779,9 @@ fwd_bf16_4w_kernel(const FwdArgs a) {
         cursor_next(a, at, ld);
     };
     if (T > 0) issue(lds0);
-    wait_vmem<0>();
+    // the Q and state loads and the first tile's copies are in flight
+    // together; this compiler-visible wait covers both
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     __syncthreads();
 
     auto v_frag = [&](const lds_char* vt, int i) -> u32x4 {
