@@ -369,28 +369,31 @@ def test_classify_respects_key_offset():
 
 # ---- O4: gradients of the definition --------------------------------------
 
-def _loss(q, k, v, dout, q_off, causal):
+def _loss(q, k, v, dout, q_off, causal, k_off=0):
     """sum(out * dout) with out from O1 (fp64 on the stored inputs)."""
     B, Tq, Hq, D = q.shape
-    o, _ = oracle.attention(q, k, v, q_off=q_off, causal=causal)
+    o, _ = oracle.attention(q, k, v, q_off=q_off, k_off=k_off, causal=causal)
     # O1 rows come b-major, then head, then position
     o = o.reshape(B, Hq, Tq, D).transpose(0, 2, 1, 3)
     return float((o * dout.astype(np.float64)).sum())
 
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_o4_matches_finite_differences(causal):
+@pytest.mark.parametrize("causal,k_off", [(True, 0), (False, 0), (True, 4)])
+def test_o4_matches_finite_differences(causal, k_off):
     """Central differences of sum(out * dout) through O1, element by element
     on a sample of q, k and v entries (perturbations taken exactly as the
-    difference of the two stored fp32 values)."""
-    rng = np.random.default_rng(41 + causal)
+    difference of the two stored fp32 values). With k_off = 4 the keys sit
+    at positions 4..10, so the causal rule compares global positions: the
+    query at 3 sees no key (no gradient), the one at 7 sees four."""
+    rng = np.random.default_rng(41 + causal + k_off)
     B, Tq, Tk, Hq, Hkv, D = 1, 5, 7, 4, 2, 8
     q = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
     k = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
     v = rng.standard_normal((B, Tk, Hkv, D)).astype(np.float32)
     dout = rng.standard_normal((B, Tq, Hq, D)).astype(np.float32)
-    q_off = 3   # queries at 3..7 see keys 0..min(i, 6) when causal
-    dq, dk, dv = oracle.attention_backward(q, k, v, dout, q_off=q_off, causal=causal)
+    q_off = 3   # queries at 3..7 see keys up to their own position when causal
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, q_off=q_off, k_off=k_off,
+                                           causal=causal)
     eps = 1.0 / 512
     for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
         idx = list(np.ndindex(x.shape))
@@ -401,8 +404,10 @@ def test_o4_matches_finite_differences(causal):
             xm[e] = np.float32(x[e] - eps)
             h = float(xp[e]) - float(xm[e])
             args = {"q": q, "k": k, "v": v}
-            lp = _loss(*[xp if n == name else args[n] for n in ("q", "k", "v")], dout, q_off, causal)
-            lm = _loss(*[xm if n == name else args[n] for n in ("q", "k", "v")], dout, q_off, causal)
+            lp = _loss(*[xp if n == name else args[n] for n in ("q", "k", "v")], dout, q_off,
+                       causal, k_off)
+            lm = _loss(*[xm if n == name else args[n] for n in ("q", "k", "v")], dout, q_off,
+                       causal, k_off)
             fd = (lp - lm) / h
             assert abs(fd - g[e]) <= 2e-5 * max(1.0, abs(fd)), (name, e, fd, g[e])
 
