@@ -124,7 +124,7 @@ def calibrate_copy(nbytes: int):
 class ClockSampler:
     """Samples the GPU's graphics clock (amdsmi GPU metrics) from a host thread
     while the timed steps run, so the line can say at what clock the chip ran
-    (the matrix cores' rate follows it, and it varies from box to box under
+    (the matrix cores' rate follows it, and it varies from chip to chip under
     the board's power limit). Reports nothing where amdsmi is not usable."""
 
     def __init__(self, period_s: float = 0.05):

@@ -160,9 +160,9 @@ int launch_fwd(const cakv::FwdArgs& a, int dtype, int D, void* stream) {
 // each split at least one tile. Few, long splits read the history fastest:
 // 768 waves in all (192 workgroups of four kv heads, on three quarters of the
 // CUs) when heads are grouped, 512 single-head waves otherwise. Measured on
-// the million-token history, one box, four-head workgroups: 512 waves
+// the million-token history, one MI355X, four-head workgroups: 512 waves
 // 5,958-5,969 GB/s, 640 6,696-6,710, 768 6,935-6,940, 896 6,819-6,822, 1,024
-// 6,738-6,747, 1,536 6,256-6,259 (another box: 2,048 6,115-6,154, 3,072
+// 6,738-6,747, 1,536 6,256-6,259 (another MI355X: 2,048 6,115-6,154, 3,072
 // 6,068-6,074, 4,096 6,001-6,020); single-head waves 512 6,686, 1,536 5,957.
 struct DecodePlan {
     int nrb;               // 32-row blocks per (batch, kv head)

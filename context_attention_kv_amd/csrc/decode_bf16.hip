@@ -492,7 +492,7 @@ int launch_split(const DecArgs& args, int D, hipStream_t s) {
 // Four or two kv heads per workgroup with two tile buffers per wave (128 or
 // 64 KB of LDS at d = 128), or one with three (48 KB). Measured on the
 // million-token history (32 query heads on 8, one new token), each against
-// the one-head, three-buffer kernel on one box: four heads 6,208-6,249 GB/s
+// the one-head, three-buffer kernel on one MI355X: four heads 6,208-6,249 GB/s
 // against 5,983-5,987 at the same split count, two heads with three buffers
 // 6,121, two heads with two 6,034-6,046; issuing the next tile before the
 // wait +0.3 %.
